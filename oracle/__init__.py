@@ -1,0 +1,271 @@
+"""Python face of the plain CPU oracle (``w8a8_oracle.c``) for the W8A8 linear layer.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the package smoke check and by the
+benchmark's CPU-baseline leg.  The GPU library never imports, links or calls it, and it shares no
+code with the GPU library; the two meet only on the seeded inputs from ``synth``.
+
+Functions take numpy arrays as stored in memory (float32, or bf16 as uint16 bit patterns) and
+return numpy arrays.  Each wrapper names the page section its C function follows; the C file's
+header lists the readings taken where the pages leave a step open.
+
+Parity of every function here is pinned by ``tests/test_oracle_*.py`` against the pages' worked
+examples, closed forms, library routines (numpy / torch casts) and brute force.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIB_PATH, build
+
+F32, BF16 = 0, 1
+INT8, FP8_E4M3 = 0, 1
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        build()
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    D, F = ctypes.c_double, ctypes.c_float
+    sig = {
+        "oracle_rounding_is_nearest": (I, []),
+        "oracle_absmax_cols": (None, [P, I, I64, I64, P]),
+        "oracle_absmax_rows": (None, [P, I, I64, I64, P]),
+        "oracle_smooth_factor": (F, [F, F, D]),
+        "oracle_smooth_factors": (None, [P, P, I64, D, P]),
+        "oracle_smooth_act": (None, [P, I, I64, I64, P, P]),
+        "oracle_smooth_weight": (None, [P, I, I64, I64, P, P]),
+        "oracle_e4m3_decode": (D, [ctypes.c_uint8]),
+        "oracle_e4m3_encode": (ctypes.c_uint8, [F]),
+        "oracle_quantize_rows": (None, [P, I64, I64, I, P, P]),
+        "oracle_quant_act": (I, [P, I, I64, I64, P, I, P, P]),
+        "oracle_fold_quant_weight": (I, [P, I, I64, I64, P, I, P, P]),
+        "oracle_gemm_i32": (I, [P, P, I64, I64, I64, P]),
+        "oracle_bf16_rne": (ctypes.c_uint16, [F]),
+        "oracle_dequant_i32": (None, [P, P, P, I64, I64, P, P]),
+        "oracle_gemm_fp8": (I, [P, P, I64, I64, I64, P, P, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if not lib.oracle_rounding_is_nearest():
+        raise RuntimeError("oracle requires round-to-nearest-even")
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _input(a):
+    """(contiguous array, dtype code) for an input stored as float32 or bf16 bits (uint16)."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return a, F32
+    if a.dtype == np.uint16:
+        return a, BF16
+    raise TypeError(f"oracle inputs are float32 or bf16 bit patterns (uint16), got {a.dtype}")
+
+
+def _f32(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float32)
+
+
+def qtype_code(q) -> int:
+    if q in (INT8, "int8"):
+        return INT8
+    if q in (FP8_E4M3, "fp8", "fp8_e4m3", "e4m3"):
+        return FP8_E4M3
+    raise ValueError(q)
+
+
+# --- calibration maxima and smoothing factors (Weight-Activation Quantization, s3) ----------
+
+def absmax_cols(x):
+    """ax[j] = max_i |X[i, j]| for X [M, K]."""
+    lib = _load()
+    x, dt = _input(x)
+    M, K = x.shape
+    ax = np.empty(K, np.float32)
+    lib.oracle_absmax_cols(_ptr(x), dt, M, K, _ptr(ax))
+    return ax
+
+
+def absmax_rows(w):
+    """aw[j] = max_n |W[j, n]| for W [K, N]."""
+    lib = _load()
+    w, dt = _input(w)
+    K, N = w.shape
+    aw = np.empty(K, np.float32)
+    lib.oracle_absmax_rows(_ptr(w), dt, K, N, _ptr(aw))
+    return aw
+
+
+def smooth_factors(ax, aw, alpha=0.5):
+    """s_j = ax_j^alpha / aw_j^(1 - alpha); s_j = 1 where either maximum is zero."""
+    lib = _load()
+    ax, aw = _f32(ax), _f32(aw)
+    s = np.empty(ax.shape[0], np.float32)
+    lib.oracle_smooth_factors(_ptr(ax), _ptr(aw), ax.shape[0], float(alpha), _ptr(s))
+    return s
+
+
+def smooth_scales(x, w, alpha=0.5):
+    """(ax, aw, s) from calibration activations X [M, K] and weights W [K, N]."""
+    ax, aw = absmax_cols(x), absmax_rows(w)
+    return ax, aw, smooth_factors(ax, aw, alpha)
+
+
+def smooth_factor(ax, aw, alpha=0.5):
+    return float(_load().oracle_smooth_factor(float(ax), float(aw), float(alpha)))
+
+
+def smooth_act(x, s=None):
+    """X~ = X diag(1/s) in float32 (division per channel)."""
+    lib = _load()
+    x, dt = _input(x)
+    M, K = x.shape
+    out = np.empty((M, K), np.float32)
+    lib.oracle_smooth_act(_ptr(x), dt, M, K, _ptr(_f32(s)), _ptr(out))
+    return out
+
+
+def smooth_weight(w, s=None):
+    """W~ = diag(s) W in float32."""
+    lib = _load()
+    w, dt = _input(w)
+    K, N = w.shape
+    out = np.empty((K, N), np.float32)
+    lib.oracle_smooth_weight(_ptr(w), dt, K, N, _ptr(_f32(s)), _ptr(out))
+    return out
+
+
+# --- quantization (s2 INT8, s4 FP8) ----------------------------------------------------------
+
+def _codes(buf, q):
+    return buf.view(np.int8) if q == INT8 else buf
+
+
+def quantize_rows(v, qtype="int8"):
+    """Per-row symmetric quantization of a float32 matrix; returns (codes, scales)."""
+    lib = _load()
+    q = qtype_code(qtype)
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    if v.ndim == 1:
+        v = v[None, :]
+    R, C = v.shape
+    codes = np.empty((R, C), np.uint8)
+    sc = np.empty(R, np.float32)
+    lib.oracle_quantize_rows(_ptr(v), R, C, q, _ptr(codes), _ptr(sc))
+    return _codes(codes, q), sc
+
+
+def quant_act(x, s=None, qtype="int8"):
+    """X [M, K] -> (codes [M, K], per-token scales [M]) after dividing by s."""
+    lib = _load()
+    q = qtype_code(qtype)
+    x, dt = _input(x)
+    M, K = x.shape
+    codes = np.empty((M, K), np.uint8)
+    sx = np.empty(M, np.float32)
+    if lib.oracle_quant_act(_ptr(x), dt, M, K, _ptr(_f32(s)), q, _ptr(codes), _ptr(sx)) != 0:
+        raise MemoryError("oracle_quant_act")
+    return _codes(codes, q), sx
+
+
+def fold_quant_weight(w, s=None, qtype="int8"):
+    """W [K, N] -> (codes [N, K], per-output-channel scales [N]) after multiplying by s."""
+    lib = _load()
+    q = qtype_code(qtype)
+    w, dt = _input(w)
+    K, N = w.shape
+    codes = np.empty((N, K), np.uint8)
+    sw = np.empty(N, np.float32)
+    if lib.oracle_fold_quant_weight(_ptr(w), dt, K, N, _ptr(_f32(s)), q, _ptr(codes), _ptr(sw)) != 0:
+        raise MemoryError("oracle_fold_quant_weight")
+    return _codes(codes, q), sw
+
+
+def e4m3_decode(code: int) -> float:
+    return float(_load().oracle_e4m3_decode(int(code) & 0xFF))
+
+
+def e4m3_encode(v: float) -> int:
+    return int(_load().oracle_e4m3_encode(float(v)))
+
+
+def bf16_rne(v: float) -> int:
+    return int(_load().oracle_bf16_rne(float(v)))
+
+
+# --- GEMM and dequantize (s3 step 2; s4) ----------------------------------------------------
+
+def gemm_i32(qx, qw):
+    """acc [M, N] = qx [M, K] @ qw [N, K]^T, exact."""
+    lib = _load()
+    qx = np.ascontiguousarray(qx, dtype=np.int8)
+    qw = np.ascontiguousarray(qw, dtype=np.int8)
+    M, K = qx.shape
+    N, K2 = qw.shape
+    assert K == K2
+    acc = np.empty((M, N), np.int32)
+    if lib.oracle_gemm_i32(_ptr(qx), _ptr(qw), M, N, K, _ptr(acc)) != 0:
+        raise OverflowError("int32 accumulator overflow")
+    return acc
+
+
+def dequant_i32(acc, sx, sw):
+    """(y64 float64 [M, N], y_bf16 uint16 [M, N]) from int32 accumulators and scales."""
+    lib = _load()
+    acc = np.ascontiguousarray(acc, dtype=np.int32)
+    M, N = acc.shape
+    y64 = np.empty((M, N), np.float64)
+    yb = np.empty((M, N), np.uint16)
+    lib.oracle_dequant_i32(_ptr(acc), _ptr(_f32(sx)), _ptr(_f32(sw)), M, N, _ptr(y64), _ptr(yb))
+    return y64, yb
+
+
+def gemm_fp8(qx, qw, sx, sw):
+    """Exact E4M3 dot products, scaled: returns (y64, mag64), both float64 [M, N]."""
+    lib = _load()
+    qx = np.ascontiguousarray(qx, dtype=np.uint8)
+    qw = np.ascontiguousarray(qw, dtype=np.uint8)
+    M, K = qx.shape
+    N, K2 = qw.shape
+    assert K == K2
+    y64 = np.empty((M, N), np.float64)
+    mag = np.empty((M, N), np.float64)
+    if lib.oracle_gemm_fp8(_ptr(qx), _ptr(qw), M, N, K, _ptr(_f32(sx)), _ptr(_f32(sw)),
+                           _ptr(y64), _ptr(mag)) != 0:
+        raise ValueError("NaN code in FP8 operands or K too large")
+    return y64, mag
+
+
+def layer(x, w, alpha=0.5, qtype="int8"):
+    """The whole path on the CPU: calibration on X itself, fold, quantize, GEMM, dequantize.
+
+    Returns a dict with every intermediate (ax, aw, s, qw, sw, qx, sx, acc or y64 ...).
+    """
+    q = qtype_code(qtype)
+    ax, aw, s = smooth_scales(x, w, alpha)
+    qw, sw = fold_quant_weight(w, s, q)
+    qx, sx = quant_act(x, s, q)
+    out = dict(ax=ax, aw=aw, s=s, qw=qw, sw=sw, qx=qx, sx=sx)
+    if q == INT8:
+        acc = gemm_i32(qx, qw)
+        y64, yb = dequant_i32(acc, sx, sw)
+        out.update(acc=acc, y64=y64, y_bf16=yb)
+    else:
+        y64, mag = gemm_fp8(qx, qw, sx, sw)
+        out.update(y64=y64, mag64=mag)
+    return out

@@ -1,0 +1,30 @@
+"""Build the plain C oracle into ``oracle/liboracle.so`` with gcc (test infrastructure only).
+
+Flags keep IEEE semantics: no fast-math, no FMA contraction, round-to-nearest default.
+OpenMP only splits independent output rows of the GEMMs.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "w8a8_oracle.c")
+LIB_PATH = os.path.join(HERE, "liboracle.so")
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off",
+          "-frounding-math", "-fopenmp", "-Wall", "-Wextra"]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB_PATH + f".tmp{os.getpid()}"
+    cmd = ["gcc", *CFLAGS, SRC, "-o", tmp, "-lm"]
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

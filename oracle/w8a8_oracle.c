@@ -1,0 +1,297 @@
+/*
+ * Plain CPU oracle for the W8A8 linear layer: SmoothQuant smoothing, symmetric per-token /
+ * per-output-channel quantization (INT8, or OCP FP8 E4M3), the integer GEMM and the dequantize.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the independent checker of the GPU library: it is
+ * loaded by the tests, by the package's smoke check and by the benchmark's CPU-baseline leg,
+ * never by the library itself.  It shares no code, header or table with the HIP kernels.
+ *
+ * Sources (web pages; sections as titled on each page):
+ *   [WAQ]  "Weight-Activation Quantization" (infra.bea.ai inference guide)
+ *            s2 "The Problem: Activation Outliers"  - symmetric INT8, scale = absmax / 127
+ *            s3 "SmoothQuant: The Smoothing Trick"  - Y = XW = (X S^-1)(S W); divide activation
+ *                                                    channel j by s_j, multiply weight channel j
+ *                                                    by s_j; two-step pipeline; s_j formula
+ *            s4 "FP8 W8A8"                          - E4M3 for weights/activations, range +-448,
+ *                                                    q = cast_fp8(x / s), s = max|x| / 448
+ *   [ACT]  "Define activation quantization..." (zenaique flashcard) - per-token / per-channel
+ *            scaling of activations and weights.
+ *
+ * Readings where the pages leave a step open (each is listed with its reason in the design notes):
+ *   - division is IEEE fp32 division, not a multiply by a reciprocal ("divide each activation
+ *     channel by s_j");
+ *   - the rounding of quantize() is round-half-to-even; INT8 codes are clamped to [-127, 127];
+ *   - X gets one scale per row (token), W~ one scale per output channel (column of W [K, N]);
+ *   - "channel j" of s_j is the contraction index: column j of X, row j of W [K, N];
+ *   - a zero maximum gives s_j = 1, and an all-zero row/column gets scale 0 and codes 0;
+ *   - alpha = 0.5 is evaluated as sqrtf(ax) / sqrtf(aw) (two correctly rounded roots and one
+ *     division); other alpha use pow in double, rounded once to float;
+ *   - dequantize is y = ((float)acc * sx[m]) * sw[n], rounded to bf16 (nearest even); the
+ *     reference value y64 = acc * sx * sw is also returned in double;
+ *   - E4M3 is the OCP "fn" flavour: bias 7, largest finite 448, subnormals m * 2^-9, no
+ *     infinities; values are clamped to [-448, 448] before rounding.
+ *
+ * Arithmetic: IEEE binary32/binary64, round-to-nearest-even, compiled without fast-math and
+ * without FMA contraction.  Every loop is the definition written out; the only parallelism is an
+ * optional OpenMP split over independent output rows, which does not change any result.
+ */
+#include <fenv.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+#define ORACLE_INT8 0
+#define ORACLE_FP8_E4M3 1
+
+/* Element i of an input stored as float32 or as bfloat16 bit patterns.  Widening bf16 to f32 is
+ * exact: the 16 bits are the high half of the float32. */
+static float load_elem(const void* p, int dtype, int64_t i) {
+    if (dtype == ORACLE_F32) return ((const float*)p)[i];
+    uint32_t u = (uint32_t)((const uint16_t*)p)[i] << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+int oracle_rounding_is_nearest(void) { return fegetround() == FE_TONEAREST; }
+
+/* ---------------------------------------------------------------------------------------------
+ * Calibration maxima, [WAQ] s3 "Choosing the Smoothing Factor": max|X_j| over the tokens of
+ * activation channel j, and max|W_j| over the outputs fed by weight channel j.
+ * ------------------------------------------------------------------------------------------- */
+void oracle_absmax_cols(const void* x, int dtype, int64_t M, int64_t K, float* ax) {
+    for (int64_t j = 0; j < K; ++j) {
+        float m = 0.0f;
+        for (int64_t i = 0; i < M; ++i) {
+            float a = fabsf(load_elem(x, dtype, i * K + j));
+            if (a > m) m = a;
+        }
+        ax[j] = m;
+    }
+}
+
+void oracle_absmax_rows(const void* w, int dtype, int64_t K, int64_t N, float* aw) {
+    for (int64_t j = 0; j < K; ++j) {
+        float m = 0.0f;
+        for (int64_t n = 0; n < N; ++n) {
+            float a = fabsf(load_elem(w, dtype, j * N + n));
+            if (a > m) m = a;
+        }
+        aw[j] = m;
+    }
+}
+
+/* s_j = max|X_j|^alpha / max|W_j|^(1 - alpha), [WAQ] s3. */
+float oracle_smooth_factor(float ax, float aw, double alpha) {
+    if (ax == 0.0f || aw == 0.0f) return 1.0f;
+    if (alpha == 0.5) return sqrtf(ax) / sqrtf(aw);
+    if (alpha == 1.0) return ax;
+    if (alpha == 0.0) return 1.0f / aw;
+    return (float)(pow((double)ax, alpha) / pow((double)aw, 1.0 - alpha));
+}
+
+void oracle_smooth_factors(const float* ax, const float* aw, int64_t K, double alpha, float* s) {
+    for (int64_t j = 0; j < K; ++j) s[j] = oracle_smooth_factor(ax[j], aw[j], alpha);
+}
+
+/* X~ = X diag(s)^-1: each activation channel j divided by s_j ([WAQ] s3).  s == NULL means s = 1. */
+void oracle_smooth_act(const void* x, int dtype, int64_t M, int64_t K, const float* s, float* xs) {
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < K; ++j) {
+            float v = load_elem(x, dtype, i * K + j);
+            xs[i * K + j] = s ? v / s[j] : v;
+        }
+}
+
+/* W~ = diag(s) W: each weight channel (row j of W [K, N]) multiplied by s_j ([WAQ] s3). */
+void oracle_smooth_weight(const void* w, int dtype, int64_t K, int64_t N, const float* s, float* ws) {
+    for (int64_t j = 0; j < K; ++j)
+        for (int64_t n = 0; n < N; ++n) {
+            float v = load_elem(w, dtype, j * N + n);
+            ws[j * N + n] = s ? s[j] * v : v;
+        }
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * OCP FP8 E4M3 ([WAQ] s4: 3 mantissa bits, range +-448).  Code layout: sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits.  Exponent field 0 holds subnormals m * 2^-9; 0x7F / 0xFF are NaN and
+ * there is no infinity, so the largest finite magnitude is 1.75 * 2^8 = 448 (code 0x7E).
+ * ------------------------------------------------------------------------------------------- */
+double oracle_e4m3_decode(uint8_t c) {
+    int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    double v = (e == 0) ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* Round |v| <= 448 to the nearest E4M3 value, ties to the even mantissa, and return its code. */
+uint8_t oracle_e4m3_encode(float v) {
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (a == 0.0) return sign;
+    int e2;
+    frexp(a, &e2);              /* a = f * 2^e2 with f in [0.5, 1): a lies in [2^(e2-1), 2^e2) */
+    int e = e2 - 1;
+    if (e < -6) e = -6;         /* below the smallest normal 2^-6 the spacing stays 2^-9 */
+    double quantum = ldexp(1.0, e - 3);         /* spacing of E4M3 values in this binade */
+    double r = nearbyint(a / quantum) * quantum;  /* a / quantum is exact (power-of-two divisor) */
+    if (r == 0.0) return sign;
+    if (r < ldexp(1.0, -6))                     /* subnormal: r = m * 2^-9, m in 1..7 */
+        return sign | (uint8_t)(r / ldexp(1.0, -9));
+    int re2;
+    double f = frexp(r, &re2);                  /* r = f * 2^re2, f in [0.5, 1) */
+    int E = re2 - 1 + 7;                        /* biased exponent */
+    int m = (int)((2.0 * f - 1.0) * 8.0);       /* exact: r has at most 4 significant bits */
+    return sign | (uint8_t)((E << 3) | m);
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Symmetric quantization of each row of a float32 matrix V [R, C] with one scale per row:
+ *   INT8 ([WAQ] s2):  scale = max|v| / 127,  q = clamp(round_half_even(v / scale), -127, 127)
+ *   E4M3 ([WAQ] s4):  scale = max|v| / 448,  q = e4m3(clamp(v / scale, -448, 448))
+ * A row whose maximum is zero gets scale 0 and all-zero codes.  Codes are stored as bytes.
+ * ------------------------------------------------------------------------------------------- */
+void oracle_quantize_rows(const float* v, int64_t R, int64_t C, int qtype, uint8_t* q, float* scale) {
+    const float qmax = (qtype == ORACLE_INT8) ? 127.0f : 448.0f;
+    for (int64_t r = 0; r < R; ++r) {
+        const float* row = v + r * C;
+        float amax = 0.0f;
+        for (int64_t c = 0; c < C; ++c)
+            if (fabsf(row[c]) > amax) amax = fabsf(row[c]);
+        float sc = amax / qmax;
+        scale[r] = sc;
+        for (int64_t c = 0; c < C; ++c) {
+            uint8_t code;
+            if (amax == 0.0f) {
+                code = 0;
+            } else if (qtype == ORACLE_INT8) {
+                float t = nearbyintf(row[c] / sc);
+                if (t > 127.0f) t = 127.0f;
+                if (t < -127.0f) t = -127.0f;
+                code = (uint8_t)(int8_t)t;
+            } else {
+                float t = row[c] / sc;
+                if (t > 448.0f) t = 448.0f;
+                if (t < -448.0f) t = -448.0f;
+                code = oracle_e4m3_encode(t);
+            }
+            q[r * C + c] = code;
+        }
+    }
+}
+
+/* Activation path at inference ([WAQ] s3 step 2, per-token scales [ACT]):
+ * X~ = X / s (per channel), then per-row quantization.  q: [M, K] codes, sx: [M]. */
+int oracle_quant_act(const void* x, int dtype, int64_t M, int64_t K, const float* s, int qtype,
+                     uint8_t* q, float* sx) {
+    float* xs = (float*)malloc(sizeof(float) * (size_t)(M * K > 0 ? M * K : 1));
+    if (!xs) return -1;
+    oracle_smooth_act(x, dtype, M, K, s, xs);
+    oracle_quantize_rows(xs, M, K, qtype, q, sx);
+    free(xs);
+    return 0;
+}
+
+/* Weight path ([WAQ] s3 step 1 then step 2, per-output-channel scales [ACT]):
+ * W~ = s * W (per channel j), then one scale per output column n of W~ [K, N].
+ * The codes are returned transposed, q: [N, K] (row n holds output channel n), sw: [N]. */
+int oracle_fold_quant_weight(const void* w, int dtype, int64_t K, int64_t N, const float* s, int qtype,
+                             uint8_t* q, float* sw) {
+    float* ws = (float*)malloc(sizeof(float) * (size_t)(K * N > 0 ? K * N : 1));
+    float* wt = (float*)malloc(sizeof(float) * (size_t)(K * N > 0 ? K * N : 1));
+    if (!ws || !wt) { free(ws); free(wt); return -1; }
+    oracle_smooth_weight(w, dtype, K, N, s, ws);
+    for (int64_t j = 0; j < K; ++j)
+        for (int64_t n = 0; n < N; ++n) wt[n * K + j] = ws[j * N + n];
+    oracle_quantize_rows(wt, N, K, qtype, q, sw);
+    free(ws);
+    free(wt);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * INT8 GEMM ([WAQ] s3 step 2: Y = dequantize(X_int8 @ W_int8)):
+ *   acc[m, n] = sum_k qx[m, k] * qw[n, k], exact in integers.
+ * With |codes| <= 127, |acc| <= K * 127^2, which fits int32 for K <= 133144; the sum is kept
+ * in int64 and the function returns -1 if any result would not fit int32.
+ * ------------------------------------------------------------------------------------------- */
+int oracle_gemm_i32(const int8_t* qx, const int8_t* qw, int64_t M, int64_t N, int64_t K, int32_t* acc) {
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t m = 0; m < M; ++m) {
+        const int8_t* a = qx + m * K;
+        for (int64_t n = 0; n < N; ++n) {
+            const int8_t* b = qw + n * K;
+            int64_t t = 0;
+            for (int64_t k = 0; k < K; ++k) t += (int64_t)a[k] * (int64_t)b[k];
+            if (t > INT32_MAX || t < INT32_MIN) bad = 1;
+            acc[m * N + n] = (int32_t)t;
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/* Round a finite float to bfloat16, nearest with ties to even; returns the bit pattern. */
+uint16_t oracle_bf16_rne(float f) {
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+/* Dequantize ([WAQ] s3 step 2; per-token x per-channel scales factor out of the sum over k):
+ *   y64[m, n] = acc * sx[m] * sw[n] in double (the reference value), and
+ *   y_bf16    = bf16(((float)acc * sx[m]) * sw[n]) (the fp32 dequantize, then bf16). */
+void oracle_dequant_i32(const int32_t* acc, const float* sx, const float* sw, int64_t M, int64_t N,
+                        double* y64, uint16_t* y_bf16) {
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int32_t a = acc[m * N + n];
+            if (y64) y64[m * N + n] = (double)a * (double)sx[m] * (double)sw[n];
+            if (y_bf16) {
+                float y = ((float)a * sx[m]) * sw[n];
+                y_bf16[m * N + n] = oracle_bf16_rne(y);
+            }
+        }
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * FP8 GEMM + dequantize ([WAQ] s4: x^ = s * q).  Every finite E4M3 value is an integer multiple
+ * of 2^-9 with |multiple| <= 448 * 2^9, so each product of two decoded codes is an integer
+ * multiple of 2^-18 and a sum of K of them is held exactly in int64 (K <= 2^26).  The oracle
+ * therefore computes the exact dot product, then:
+ *   y64[m, n]  = dot * sx[m] * sw[n]                     (double; the reference value)
+ *   mag64[m,n] = sum_k |dec(qx) dec(qw)| * sx[m] * sw[n]  (for a floating-point error bound)
+ * ------------------------------------------------------------------------------------------- */
+int oracle_gemm_fp8(const uint8_t* qx, const uint8_t* qw, int64_t M, int64_t N, int64_t K,
+                    const float* sx, const float* sw, double* y64, double* mag64) {
+    int64_t lut[256];
+    for (int c = 0; c < 256; ++c) {
+        double d = oracle_e4m3_decode((uint8_t)c);
+        lut[c] = isnan(d) ? 0 : (int64_t)ldexp(d, 9);   /* decoded value in units of 2^-9 */
+    }
+    int bad = 0;
+    for (int64_t i = 0; i < M * K; ++i) bad |= ((qx[i] & 0x7F) == 0x7F);
+    for (int64_t i = 0; i < N * K; ++i) bad |= ((qw[i] & 0x7F) == 0x7F);
+    if (bad || K > ((int64_t)1 << 26)) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        const uint8_t* a = qx + m * K;
+        for (int64_t n = 0; n < N; ++n) {
+            const uint8_t* b = qw + n * K;
+            int64_t t = 0, u = 0;
+            for (int64_t k = 0; k < K; ++k) {
+                int64_t p = lut[a[k]] * lut[b[k]];
+                t += p;
+                u += p < 0 ? -p : p;
+            }
+            double scale = (double)sx[m] * (double)sw[n];
+            if (y64) y64[m * N + n] = ldexp((double)t, -18) * scale;
+            if (mag64) mag64[m * N + n] = ldexp((double)u, -18) * scale;
+        }
+    }
+    return 0;
+}
