@@ -1,0 +1,157 @@
+// Calibration reductions and SmoothQuant factors ("Weight-Activation Quantization", section 3,
+// "Choosing the Smoothing Factor": s_j = max|X_j|^alpha / max|W_j|^(1-alpha)).
+//
+// Both reductions are HBM-bound streams.  Loads are 16 bytes per lane (8 bf16 or 2x4 fp32), a
+// wave covers 512 consecutive columns of a row, and every maximum is exact (fp32 max needs no
+// rounding), so the result does not depend on how the work is split.
+#include "device.h"
+#include "launch.h"
+
+namespace w8a8 {
+
+namespace {
+
+constexpr int kColsPerWave = 8 * kWave;   // 512 columns: one 16-byte chunk of 8 elements per lane
+constexpr int kRowsPerBlock = 32;         // 4 waves x 8 rows each
+
+__global__ void fill_kernel(float* p, int64_t n, float v) {
+    int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+template <bool kBf16>
+__device__ __forceinline__ float load1(const void* base, int64_t i) {
+    if constexpr (kBf16) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(base)[i]) << 16);
+    else return static_cast<const float*>(base)[i];
+}
+
+// 8 elements starting at column c of a row; columns >= C read as 0.  kVec: the row is 16-byte
+// aligned and C is a multiple of 8, so a chunk is entirely inside or outside the row.
+template <bool kBf16, bool kVec>
+__device__ __forceinline__ void load_chunk(const void* base, int64_t row_start, int64_t c, int64_t C,
+                                           float (&v)[8]) {
+    if constexpr (kVec) {
+        load8<kBf16>(base, row_start + c, v);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (c + e < C) ? load1<kBf16>(base, row_start + c + e) : 0.0f;
+    }
+}
+
+// Column maxima of |a[r, c] * row_scale[r]| over a block of kRowsPerBlock rows and 512 columns,
+// merged across waves in LDS and across blocks with an atomic maximum.
+template <bool kBf16, bool kVec>
+__global__ __launch_bounds__(256) void absmax_cols_kernel(const void* __restrict__ a, int64_t R, int64_t C,
+                                                          const float* __restrict__ row_scale,
+                                                          float* __restrict__ out) {
+    __shared__ float part[4][kColsPerWave];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int64_t c = static_cast<int64_t>(blockIdx.x) * kColsPerWave + lane * 8;
+    const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kRowsPerBlock;
+    float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (c < C) {
+#pragma unroll
+        for (int i = 0; i < kRowsPerBlock / 4; ++i) {
+            const int64_t r = r0 + wave + 4 * i;
+            if (r < R) {
+                float v[8];
+                load_chunk<kBf16, kVec>(a, r * C, c, C, v);
+                const float rs = row_scale ? row_scale[r] : 1.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) m[e] = fmaxf(m[e], fabsf(row_scale ? rs * v[e] : v[e]));
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[wave][lane * 8 + e] = m[e];
+    __syncthreads();
+    for (int i = threadIdx.x; i < kColsPerWave; i += blockDim.x) {
+        const int64_t col = static_cast<int64_t>(blockIdx.x) * kColsPerWave + i;
+        if (col < C) {
+            float v = fmaxf(fmaxf(part[0][i], part[1][i]), fmaxf(part[2][i], part[3][i]));
+            atomic_max_nonneg(out + col, v);
+        }
+    }
+}
+
+// Row maxima: one wave per row, 16-byte chunks strided by the wave.
+template <bool kBf16, bool kVec>
+__global__ __launch_bounds__(256) void absmax_rows_kernel(const void* __restrict__ a, int64_t R, int64_t C,
+                                                          float* __restrict__ out) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+    if (r >= R) return;
+    float m = 0.0f;
+    for (int64_t c = static_cast<int64_t>(lane) * 8; c < C; c += kColsPerWave) {
+        float v[8];
+        load_chunk<kBf16, kVec>(a, r * C, c, C, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+    }
+    m = wave_max(m);
+    if (lane == 0) out[r] = m;
+}
+
+// s_j = ax^alpha / aw^(1-alpha).  alpha = 0.5: correctly rounded roots and division; alpha = 1 and
+// alpha = 0 reduce to ax and 1/aw exactly; otherwise pow in double, rounded once to fp32.
+__global__ void smooth_factors_kernel(const float* __restrict__ ax, const float* __restrict__ aw, int64_t K,
+                                      float alpha, float* __restrict__ s) {
+    int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (j >= K) return;
+    const float a = ax[j], b = aw[j];
+    float r;
+    if (a == 0.0f || b == 0.0f) r = 1.0f;
+    else if (alpha == 0.5f) r = div_rn(__builtin_sqrtf(a), __builtin_sqrtf(b));
+    else if (alpha == 1.0f) r = a;
+    else if (alpha == 0.0f) r = div_rn(1.0f, b);
+    else r = static_cast<float>(pow(static_cast<double>(a), static_cast<double>(alpha)) /
+                                pow(static_cast<double>(b), 1.0 - static_cast<double>(alpha)));
+    s[j] = r;
+}
+
+}  // namespace
+
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, p, n, v);
+    return hipGetLastError();
+}
+
+hipError_t launch_absmax_cols(const void* a, bool bf16, int64_t R, int64_t C, const float* row_scale,
+                              float* out, hipStream_t st) {
+    if (R <= 0 || C <= 0) return hipSuccess;
+    dim3 grid(static_cast<unsigned>((C + kColsPerWave - 1) / kColsPerWave),
+              static_cast<unsigned>((R + kRowsPerBlock - 1) / kRowsPerBlock));
+    const bool vec = (C % 8) == 0;
+    if (bf16) {
+        if (vec) hipLaunchKernelGGL((absmax_cols_kernel<true, true>), grid, dim3(256), 0, st, a, R, C, row_scale, out);
+        else hipLaunchKernelGGL((absmax_cols_kernel<true, false>), grid, dim3(256), 0, st, a, R, C, row_scale, out);
+    } else {
+        if (vec) hipLaunchKernelGGL((absmax_cols_kernel<false, true>), grid, dim3(256), 0, st, a, R, C, row_scale, out);
+        else hipLaunchKernelGGL((absmax_cols_kernel<false, false>), grid, dim3(256), 0, st, a, R, C, row_scale, out);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_absmax_rows(const void* a, bool bf16, int64_t R, int64_t C, float* out, hipStream_t st) {
+    if (R <= 0) return hipSuccess;
+    dim3 grid(static_cast<unsigned>((R + 3) / 4));
+    const bool vec = (C % 8) == 0;
+    if (bf16) {
+        if (vec) hipLaunchKernelGGL((absmax_rows_kernel<true, true>), grid, dim3(256), 0, st, a, R, C, out);
+        else hipLaunchKernelGGL((absmax_rows_kernel<true, false>), grid, dim3(256), 0, st, a, R, C, out);
+    } else {
+        if (vec) hipLaunchKernelGGL((absmax_rows_kernel<false, true>), grid, dim3(256), 0, st, a, R, C, out);
+        else hipLaunchKernelGGL((absmax_rows_kernel<false, false>), grid, dim3(256), 0, st, a, R, C, out);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_smooth_factors(const float* ax, const float* aw, int64_t K, float alpha, float* s,
+                                 hipStream_t st) {
+    hipLaunchKernelGGL(smooth_factors_kernel, dim3(static_cast<unsigned>((K + 255) / 256)), dim3(256), 0, st,
+                       ax, aw, K, alpha, s);
+    return hipGetLastError();
+}
+
+}  // namespace w8a8

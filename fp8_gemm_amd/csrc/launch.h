@@ -1,0 +1,44 @@
+// Host-side launchers of the libw8a8 kernels.  Arguments are validated by the C-ABI layer
+// (api.hip) before any of these is called; each returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+// Fill n floats with v (used instead of a memset so the call sequence stays capturable).
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st);
+
+// out[c] = max(out[c], max_r |a[r, c]| * (scale ? scale[r] : 1)) for a row-major [R, C] matrix of
+// float32 or bf16.  Exact; concurrent blocks merge with an order-independent atomic maximum.
+hipError_t launch_absmax_cols(const void* a, bool bf16, int64_t R, int64_t C, const float* row_scale,
+                              float* out, hipStream_t st);
+
+// out[r] = max_c |a[r, c]| for a row-major [R, C] matrix (one wave per row, no atomics).
+hipError_t launch_absmax_rows(const void* a, bool bf16, int64_t R, int64_t C, float* out, hipStream_t st);
+
+// s[j] = ax[j]^alpha / aw[j]^(1-alpha), s = 1 where a maximum is 0.
+hipError_t launch_smooth_factors(const float* ax, const float* aw, int64_t K, float alpha, float* s,
+                                 hipStream_t st);
+
+// Per-row smooth + quantize of X [M, K]: xq [M, K] codes and x_scale [M].
+hipError_t launch_quant_act(const void* x, bool bf16, int64_t M, int64_t K, const float* s, bool fp8,
+                            uint8_t* xq, float* x_scale, hipStream_t st);
+
+// Quantize W~ = s * W [K, N] with per-column maxima amax [N] (from launch_absmax_cols) and write
+// the codes transposed, wq [N, K].  amax is read, not changed.
+hipError_t launch_quant_weight_t(const void* w, bool bf16, int64_t K, int64_t N, const float* s,
+                                 const float* amax, bool fp8, uint8_t* wq, hipStream_t st);
+
+// scale[n] = amax[n] / (fp8 ? 448 : 127), in place.
+hipError_t launch_finalize_scales(float* amax_to_scale, int64_t n, bool fp8, hipStream_t st);
+
+// GEMM over K-contiguous operands xq [M, K] and wq [N, K]:
+//   acc != nullptr: the raw accumulators [M, N] (int32 for INT8, fp32 for E4M3)
+//   else: y bf16 [M, N] = ((float)acc * x_scale[m]) * w_scale[n].
+hipError_t launch_gemm(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale,
+                       bool fp8, int64_t M, int64_t N, int64_t K, uint16_t* y, void* acc,
+                       hipStream_t st);
+
+}  // namespace w8a8

@@ -1,0 +1,138 @@
+/*
+ * libw8a8 - the W8A8 linear layer on AMD Instinct MI355X (gfx950).
+ *
+ * The layer Y = X W is computed as Y = (X diag(1/s)) (diag(s) W) with SmoothQuant factors s,
+ * symmetric 8-bit quantization of both operands (one scale per token of X, one per output channel
+ * of W), an 8-bit GEMM with 32-bit accumulation on the matrix cores, and a dequantizing epilogue
+ * that writes bf16.  Sources, by page and section:
+ *   [WAQ] "Weight-Activation Quantization" (infra.bea.ai inference guide):
+ *         s2 "The Problem: Activation Outliers"  symmetric INT8, scale = absmax / 127;
+ *         s3 "SmoothQuant: The Smoothing Trick"  Y = XW = (X S^-1)(S W), divide activation
+ *             channel j by s_j and multiply weight channel j by s_j, smoothing offline then
+ *             quantization at inference, Y = dequantize(X_int8 @ W_int8), and
+ *             s_j = max|X_j|^alpha / max|W_j|^(1-alpha) with alpha in [0, 1];
+ *         s4 "FP8 W8A8"  E4M3 operands, range [-448, 448], q = cast_fp8(x / s), x^ = s q,
+ *             s = max|x| / 448.
+ *   [ACT] "Define activation quantization ..." (zenaique flashcard): per-token activation and
+ *         per-channel weight scaling.
+ *
+ * Conventions shared by every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library allocates nothing and
+ *     keeps no state between calls.  All matrices are dense and row-major.
+ *   - X is [M, K] (M tokens, K input channels); W is [K, N] (N output channels); Y is [M, N].
+ *     Quantized weights are stored transposed, [N, K], so that both GEMM operands have K
+ *     contiguous.  Codes are one byte each: int8 for W8A8_INT8, OCP E4M3 ("fn": bias 7, max 448,
+ *     no infinities) bit patterns for W8A8_FP8_E4M3.
+ *   - Element types of X and W: float32 or bfloat16.  Y is bfloat16 (round to nearest even).
+ *   - Every call is asynchronous on `stream` (0 = the default stream) and returns after queueing.
+ *   - Shapes: M >= 0 and N >= 0 (0 = nothing to do, W8A8_OK with nothing launched); K >= 1.
+ *     K must be a multiple of 16 and every pointer 16-byte aligned, else W8A8_ERR_UNSUPPORTED.
+ *   - Errors: NULL required pointer, negative size, unknown enum, alpha outside [0, 1] ->
+ *     W8A8_ERR_INVALID_ARG, checked before anything is queued; a failed launch -> W8A8_ERR_HIP.
+ *   - Arithmetic: divisions are IEEE fp32 divisions and roundings are to nearest, ties to even,
+ *     so the quantized codes, scales and int32 accumulators are deterministic and reproducible
+ *     bit for bit.  A zero maximum gives s_j = 1; an all-zero row or column gets scale 0 and
+ *     codes 0.  NaN and infinite inputs are not supported.
+ */
+#ifndef W8A8_H
+#define W8A8_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum w8a8_status {
+    W8A8_OK = 0,
+    W8A8_ERR_INVALID_ARG = 1,
+    W8A8_ERR_UNSUPPORTED = 2,
+    W8A8_ERR_HIP = 3
+} w8a8_status;
+
+typedef enum w8a8_dtype { W8A8_F32 = 0, W8A8_BF16 = 1 } w8a8_dtype;
+
+typedef enum w8a8_qtype { W8A8_INT8 = 0, W8A8_FP8_E4M3 = 1 } w8a8_qtype;
+
+/*
+ * Calibration maxima and SmoothQuant factors ([WAQ] s3 "Choosing the Smoothing Factor").
+ *   ax[j] = max_i |X[i, j]|       (column maxima of the calibration activations X [M, K])
+ *   aw[j] = max_n |W[j, n]|       (row maxima of the weights W [K, N])
+ *   s[j]  = ax[j]^alpha / aw[j]^(1 - alpha); s[j] = 1 where ax[j] or aw[j] is 0.
+ *           alpha = 0.5 is evaluated as sqrt(ax) / sqrt(aw) with correctly rounded fp32 roots and
+ *           division (bit-reproducible); other alpha use pow in double rounded once to fp32.
+ * ax, aw, s: caller-owned fp32 [K], all written.  accumulate != 0 folds the maxima of this X into
+ * the values already in ax (max over several calibration batches); 0 overwrites ax.  M may be 0
+ * (no calibration rows: ax is left as is with accumulate, else zero).
+ */
+w8a8_status w8a8_smooth_scales(const void* x, w8a8_dtype x_dtype, int64_t M, int64_t K,
+                               const void* w, w8a8_dtype w_dtype, int64_t N, float alpha,
+                               float* ax, float* aw, int accumulate, float* s, hipStream_t stream);
+
+/*
+ * Weight fold and quantize ([WAQ] s3 step 1 "W_tilde = diag(s) @ W" and step 2
+ * "W_int8 = quantize(W_tilde)"; per-output-channel scales [ACT]; FP8 per [WAQ] s4).
+ *   W~[j, n]   = s[j] * W[j, n]                               (fp32 multiply; s == NULL: s = 1)
+ *   w_scale[n] = max_j |W~[j, n]| / Q                         (Q = 127 for INT8, 448 for E4M3)
+ *   wq[n, j]   = INT8: clamp(round_half_even(W~[j, n] / w_scale[n]), -127, 127)
+ *                E4M3: e4m3_round_half_even(clamp(W~[j, n] / w_scale[n], -448, 448))
+ * w: [K, N] in w_dtype.  s: fp32 [K] or NULL.  wq: [N, K] bytes (written).  w_scale: fp32 [N]
+ * (written; also used as scratch while the call runs).
+ */
+w8a8_status w8a8_fold_quant_weight(const void* w, w8a8_dtype w_dtype, int64_t K, int64_t N,
+                                   const float* s, w8a8_qtype qtype, void* wq, float* w_scale,
+                                   hipStream_t stream);
+
+/*
+ * Activation smooth + per-token quantize, one pass over X ([WAQ] s3 "divide each activation
+ * channel by s_j" and step 2 "X_int8 = quantize(X_tilde)"; per-token scales [ACT]; FP8 [WAQ] s4).
+ *   X~[i, j]   = X[i, j] / s[j]                               (fp32 division; s == NULL: s = 1)
+ *   x_scale[i] = max_j |X~[i, j]| / Q                         (Q = 127 or 448)
+ *   xq[i, j]   = the same rounding as w8a8_fold_quant_weight, with x_scale[i].
+ * x: [M, K] in x_dtype.  s: fp32 [K] or NULL.  xq: [M, K] bytes.  x_scale: fp32 [M].
+ */
+w8a8_status w8a8_quant_act(const void* x, w8a8_dtype x_dtype, int64_t M, int64_t K,
+                           const float* s, w8a8_qtype qtype, void* xq, float* x_scale,
+                           hipStream_t stream);
+
+/*
+ * Quantized GEMM with the dequantizing epilogue ([WAQ] s3 "Y = dequantize(X_int8 @ W_int8)";
+ * [WAQ] s4 x^ = s q for E4M3).
+ *   INT8: acc[i, n] = sum_k xq[i, k] * wq[n, k] exactly in int32 (|acc| <= K * 127^2, so
+ *         K <= 133144), y[i, n] = bf16(((float)acc * x_scale[i]) * w_scale[n]).
+ *   E4M3: acc = sum_k e4m3(xq[i, k]) * e4m3(wq[n, k]) accumulated in fp32 on the matrix cores
+ *         (products are exact; the summation order is the hardware's), y as above.
+ * xq: [M, K] bytes, x_scale: fp32 [M], wq: [N, K] bytes, w_scale: fp32 [N], y: bf16 [M, N].
+ */
+w8a8_status w8a8_gemm_dequant(const void* xq, const float* x_scale, const void* wq,
+                              const float* w_scale, w8a8_qtype qtype, int64_t M, int64_t N,
+                              int64_t K, void* y, hipStream_t stream);
+
+/*
+ * The INT8 GEMM without the epilogue: acc[i, n] = sum_k xq[i, k] * wq[n, k] in int32 [M, N].
+ * Same kernels and tiling as w8a8_gemm_dequant; exists so the integer accumulators can be
+ * checked bit for bit.  K <= 133144.
+ */
+w8a8_status w8a8_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t M, int64_t N, int64_t K,
+                          int32_t* acc, hipStream_t stream);
+
+/*
+ * The E4M3 GEMM without the epilogue: acc[i, n] = sum_k e4m3(xq[i, k]) * e4m3(wq[n, k]) as the
+ * matrix cores accumulate it, fp32 [M, N].  Same kernels and tiling as w8a8_gemm_dequant with
+ * W8A8_FP8_E4M3; exists so the accumulators can be compared with an exact dot product.
+ */
+w8a8_status w8a8_gemm_f32(const uint8_t* xq, const uint8_t* wq, int64_t M, int64_t N, int64_t K,
+                          float* acc, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* w8a8_status_string(w8a8_status status);
+
+/* Static version string of the library. */
+const char* w8a8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8_H */

@@ -37,6 +37,7 @@ def _load():
     D, F = ctypes.c_double, ctypes.c_float
     sig = {
         "oracle_rounding_is_nearest": (I, []),
+        "oracle_num_threads": (I, []),
         "oracle_absmax_cols": (None, [P, I, I64, I64, P]),
         "oracle_absmax_rows": (None, [P, I, I64, I64, P]),
         "oracle_smooth_factor": (F, [F, F, D]),
@@ -61,6 +62,11 @@ def _load():
         raise RuntimeError("oracle requires round-to-nearest-even")
     _lib = lib
     return lib
+
+
+def num_threads() -> int:
+    """Threads used by the oracle's parallel loops (the GEMMs); the rest runs on one thread."""
+    return int(_load().oracle_num_threads())
 
 
 def _ptr(a):

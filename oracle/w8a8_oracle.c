@@ -40,6 +40,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
@@ -57,6 +60,15 @@ static float load_elem(const void* p, int dtype, int64_t i) {
 }
 
 int oracle_rounding_is_nearest(void) { return fegetround() == FE_TONEAREST; }
+
+/* Threads the OpenMP loops below may use (1 without OpenMP). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ---------------------------------------------------------------------------------------------
  * Calibration maxima, [WAQ] s3 "Choosing the Smoothing Factor": max|X_j| over the tokens of
