@@ -25,6 +25,7 @@ w8a8_status check_dims(int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K < 1 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return W8A8_ERR_INVALID_ARG;
     if (K % 16 != 0) return W8A8_ERR_UNSUPPORTED;
     if (M / 32 >= 65535 || K / 32 >= 65535 || K / 128 >= 65535) return W8A8_ERR_UNSUPPORTED;  // 2-D grid limits
+    if (K >= (int64_t(1) << 24)) return W8A8_ERR_UNSUPPORTED;   // 32-bit in-tile offsets of the GEMM
     return W8A8_OK;
 }
 

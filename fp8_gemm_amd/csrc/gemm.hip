@@ -2,16 +2,20 @@
 // ("Weight-Activation Quantization", section 3 step 2: Y = dequantize(X_int8 @ W_int8); section 4:
 // x^ = s q for E4M3.)
 //
-// Both operands are K-contiguous: xq [M, K] and wq [N, K].  The matrix-core instructions are
-//   INT8: v_mfma_i32_16x16x64_i8          (int32 accumulate, exact)
-//   E4M3: v_mfma_f32_16x16x128_f8f6f4     (fp32 accumulate; e4m3 x e4m3 products are exact)
+// Both operands are K-contiguous: xq [M, K] and wq [N, K].  Matrix-core instructions:
+//   INT8: v_mfma_i32_32x32x32_i8            (large-M kernel; int32 accumulate, exact)
+//         v_mfma_i32_16x16x64_i8            (small-M kernel)
+//   E4M3: v_mfma_f32_32x32x64_f8f6f4        (large-M kernel)
+//         v_mfma_f32_16x16x128_f8f6f4       (small-M kernel)
+//         fp32 accumulate; e4m3 x e4m3 products are exact, the summation is the hardware's.
 // Each lane feeds 16 (INT8) or 32 (E4M3) consecutive K bytes of one row of each operand; the
-// instruction pairs the bytes of A and B the same way, so any assignment of K to lanes that is
-// the same for both operands gives the full dot product.
+// instruction pairs the bytes of A and B the same way, so any assignment of K to lanes that is the
+// same for both operands gives the full dot product.
 //
-// The W tile is the instruction's A operand and the X tile its B operand, so the 16x16 result
-// block held by a lane is Y[m = lane % 16][n = 4 * (lane / 16) + r], r = 0..3: four consecutive
-// outputs of one row, stored as one 8-byte write after the epilogue.
+// The W tile is the instruction's A operand and the X tile its B operand, so a lane's results are
+// runs of four consecutive outputs n of one row m, which the epilogue stores as 8-byte writes:
+//   16x16 block: m = lane % 16, n = 4 * (lane / 16) + r                      (r = 0..3)
+//   32x32 block: m = lane % 32, n = 8 * g + 4 * (lane / 32) + r, acc[4g + r]  (g, r = 0..3)
 #include <type_traits>
 
 #include "device.h"
@@ -21,50 +25,238 @@ namespace w8a8 {
 
 namespace {
 
-// ------------------------------------------------------------------------------------------------
-// Large-M kernel: block tile kBM x kBN, K step 128 bytes, 4 waves in a 2 x 2 grid, each wave
-// kBM/2 x kBN/2.  Tiles are staged global -> registers -> LDS with two LDS buffers (one barrier per
-// K step).  LDS rows are 128 bytes = 8 chunks of 16 bytes; chunk c of row r is stored at position
-// c ^ (r & 7), so the 8 lanes of a 128-byte LDS phase (8 consecutive rows, same chunk) hit 8
-// different bank groups on both the writes and the fragment reads.
-// ------------------------------------------------------------------------------------------------
-constexpr int kBK = 128;
-constexpr int kThreads = 256;
+constexpr int kBK = 128;        // K bytes per pipeline stage
+constexpr int kThreads = 256;   // 4 waves
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 4); }
+typedef float v16f __attribute__((ext_vector_type(16)));
 
-template <int kRows>
-struct TileLoad {
-    static constexpr int kPerThread = kRows * (kBK / 16) / kThreads;
-    v4i reg[kPerThread];
+// ---- matrix-core instruction wrappers ------------------------------------------------------------
 
-    // Rows beyond `rows` re-read the last valid row (their results are never stored); chunks at
-    // or beyond K read as zero, which adds nothing to any dot product.
-    __device__ __forceinline__ void load(const uint8_t* __restrict__ g, int64_t row0, int64_t rows, int64_t K,
-                                         int64_t k0, bool full_k) {
+// kTile: block edge; kKStep: K bytes per instruction; kChunks: 16-byte chunks per lane per
+// instruction; kGroups: runs of four outputs per lane.
+struct MmaI8x16 {               // v_mfma_i32_16x16x64_i8
+    using Acc = v4i;
+    static constexpr int kTile = 16, kKStep = 64, kChunks = 1, kGroups = 1;
+    __device__ static __forceinline__ Acc zero() { return Acc{0, 0, 0, 0}; }
+    __device__ static __forceinline__ Acc run(const v4i* a, const v4i* b, Acc c) {
+        return __builtin_amdgcn_mfma_i32_16x16x64_i8(a[0], b[0], c, 0, 0, 0);
+    }
+};
+
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+struct MmaI8x32 {               // v_mfma_i32_32x32x32_i8
+    using Acc = v16i;
+    static constexpr int kTile = 32, kKStep = 32, kChunks = 1, kGroups = 4;
+    __device__ static __forceinline__ Acc zero() { return Acc{}; }
+    __device__ static __forceinline__ Acc run(const v4i* a, const v4i* b, Acc c) {
+        return __builtin_amdgcn_mfma_i32_32x32x32_i8(a[0], b[0], c, 0, 0, 0);
+    }
+};
+
+__device__ __forceinline__ v8i cat(const v4i* p) {
+    return v8i{p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2], p[1][3]};
+}
+
+struct MmaF8x16 {               // v_mfma_f32_16x16x128_f8f6f4, both operands E4M3
+    using Acc = v4f;
+    static constexpr int kTile = 16, kKStep = 128, kChunks = 2, kGroups = 1;
+    __device__ static __forceinline__ Acc zero() { return Acc{0.f, 0.f, 0.f, 0.f}; }
+    __device__ static __forceinline__ Acc run(const v4i* a, const v4i* b, Acc c) {
+        // format codes 0, 0: both operands OCP E4M3; zero scale operands select the unscaled form.
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cat(a), cat(b), c, 0, 0, 0, 0, 0, 0);
+    }
+};
+
+struct MmaF8x32 {               // v_mfma_f32_32x32x64_f8f6f4, both operands E4M3
+    using Acc = v16f;
+    static constexpr int kTile = 32, kKStep = 64, kChunks = 2, kGroups = 4;
+    __device__ static __forceinline__ Acc zero() { return Acc{}; }
+    __device__ static __forceinline__ Acc run(const v4i* a, const v4i* b, Acc c) {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(a), cat(b), c, 0, 0, 0, 0, 0, 0);
+    }
+};
+
+// Row m and first column n of group g of a lane's results in a kTile x kTile block.
+template <int kTile>
+__device__ __forceinline__ int out_row(int lane) { return lane % kTile; }
+template <int kTile>
+__device__ __forceinline__ int out_col(int lane, int g) {
+    return kTile == 16 ? 4 * (lane / 16) : 8 * g + 4 * (lane / 32);
+}
+
+// Dequantize and store four consecutive outputs of row m starting at column n (or store the raw
+// accumulators when kOutAcc).
+template <bool kOutAcc, typename T>
+__device__ __forceinline__ void store4(const T (&a)[4], int64_t m, int64_t n, int64_t M, int64_t N, float sxm,
+                                       const float* __restrict__ w_scale, uint16_t* __restrict__ y,
+                                       void* __restrict__ out_acc) {
+    if (m >= M) return;
+    if constexpr (kOutAcc) {
+        T* p = static_cast<T*>(out_acc) + m * N + n;
+        if (n + 3 < N && (N & 3) == 0) {
+            typedef T v4t __attribute__((ext_vector_type(4)));
+            *reinterpret_cast<v4t*>(p) = v4t{a[0], a[1], a[2], a[3]};
+        } else {
 #pragma unroll
-        for (int i = 0; i < kPerThread; ++i) {
-            const int idx = threadIdx.x + kThreads * i;
-            const int r = idx >> 3, c = idx & 7;
-            int64_t gr = row0 + r;
-            gr = gr < rows ? gr : rows - 1;
-            const int64_t k = k0 + c * 16;
-            if (full_k || k < K) reg[i] = *reinterpret_cast<const v4i*>(g + gr * K + k);
-            else reg[i] = v4i{0, 0, 0, 0};
+            for (int r = 0; r < 4; ++r)
+                if (n + r < N) p[r] = a[r];
+        }
+    } else {
+        uint32_t h[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float swn = (n + r < N) ? w_scale[n + r] : 0.0f;
+            h[r] = bf16_bits((static_cast<float>(a[r]) * sxm) * swn);
+        }
+        uint16_t* p = y + m * N + n;
+        if (n + 3 < N && (N & 3) == 0) {
+            *reinterpret_cast<uint2*>(p) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (n + r < N) p[r] = static_cast<uint16_t>(h[r]);
         }
     }
-    __device__ __forceinline__ void store(uint8_t* lds) const {
+}
+
+// Epilogue of one kTile x kTile accumulator block whose rows start at m_base and columns at n_base.
+template <typename MM, bool kOutAcc>
+__device__ __forceinline__ void store_block(const typename MM::Acc& acc, int64_t m_base, int64_t n_base, int lane,
+                                            int64_t M, int64_t N, const float* __restrict__ x_scale,
+                                            const float* __restrict__ w_scale, uint16_t* __restrict__ y,
+                                            void* __restrict__ out_acc) {
+    using T = typename std::remove_cv<typename std::remove_reference<decltype(acc[0])>::type>::type;
+    const int64_t m = m_base + out_row<MM::kTile>(lane);
+    const float sxm = (!kOutAcc && m < M) ? x_scale[m] : 0.0f;
 #pragma unroll
-        for (int i = 0; i < kPerThread; ++i) {
-            const int idx = threadIdx.x + kThreads * i;
-            *reinterpret_cast<v4i*>(lds + swz(idx >> 3, idx & 7)) = reg[i];
+    for (int g = 0; g < MM::kGroups; ++g) {
+        const T a[4] = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+        store4<kOutAcc>(a, m, n_base + out_col<MM::kTile>(lane, g), M, N, sxm, w_scale, y, out_acc);
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Large-M kernel: block tile kBM x kBN, 4 waves in a 2 x 2 grid, each wave kBM/2 x kBN/2.
+//
+// LDS holds three stages per operand, each one K step of 128 bytes per row.  A row is 8 chunks of
+// 16 bytes, stored in the swizzled order of swz() so that fragment reads are free of bank
+// conflicts.
+//
+// Stages are filled by direct global -> LDS copies (global_load_lds_dwordx4).  The copies are
+// written as inline assembly so that the compiler's wait-count pass does not serialise them with
+// the fragment reads of other stages; ordering is explicit: a wave waits (s_waitcnt vmcnt) for its
+// own copies of a stage, then the block meets at a barrier.
+//
+// Schedule of K step kt (each half-step h = K bytes [64h, 64h + 64) of the stage):
+//   read fragments of half 1 of stage kt    | 512 matrix-core cycles of half 0 of stage kt
+//   wait for stage kt + 1, barrier, copy K step kt + 3 into the stage of kt (now fully read)
+//   read fragments of half 0 of stage kt+1  | 512 matrix-core cycles of half 1 of stage kt
+// so fragment reads overlap the matrix cores and copies run three K steps ahead.
+// ------------------------------------------------------------------------------------------------
+
+// 16 zero bytes: the source of copies for K positions beyond the end of a row.
+__device__ __attribute__((aligned(16))) uint8_t g_zero16[16] = {0};
+
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int kN>
+__device__ __forceinline__ void wait_copies() {
+    static_assert(kN >= 0 && kN < 64, "vmcnt is a 6-bit counter");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kN) : "memory");
+}
+
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Byte address of a __shared__ object inside the block's LDS allocation (what M0 expects).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    const __attribute__((address_space(3))) void* l = (const __attribute__((address_space(3))) void*)(p);
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(l));
+}
+
+// One 16-byte-per-lane copy into LDS bytes [lds, lds + 1024): lane l writes lds + 16 l.
+__device__ __forceinline__ void copy_sv(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "global_load_lds_dwordx4 %1, %2"
+        :
+        : "s"(lds), "v"(voff), "s"(sbase)
+        : "memory", "m0");
+}
+__device__ __forceinline__ void copy_v(uintptr_t src, uint32_t lds) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "global_load_lds_dwordx4 %1, off"
+        :
+        : "s"(lds), "v"(src)
+        : "memory", "m0");
+}
+
+// Copies of one K step of a tile: kRows rows x 128 bytes.  One wave instruction fills 1 KB of LDS
+// (8 rows): lane l lands at row l / 8 of the block, stored chunk l % 8, which holds the logical
+// chunk that swz() places there.  A lane's source offset inside the tile is fixed for the whole K
+// loop.  Rows
+// past the end re-read the last row (never stored); in the last K step of a ragged K, chunks past
+// K come from g_zero16.
+template <int kRows>
+struct CopyPlan {
+    static constexpr int kPerWave = kRows / 32;
+    uint32_t off[kPerWave];
+    int chunk;
+
+    __device__ __forceinline__ void init(int64_t row0, int64_t rows, int64_t K, int wave, int lane) {
+        const int rl = lane >> 3;
+        // copy i of this wave fills rows 8 * blk + rl, blk = wave + 4 i (so blk is odd iff wave is);
+        // its stored chunk lane % 8 holds logical chunk (lane % 8) ^ ((row >> 1) & 7).
+        chunk = (lane & 7) ^ ((4 * (wave & 1) + (rl >> 1)) & 7);
+#pragma unroll
+        for (int i = 0; i < kPerWave; ++i) {
+            int64_t gr = row0 + (wave + 4 * i) * 8 + rl;
+            gr = gr < rows ? gr : rows - 1;
+            off[i] = static_cast<uint32_t>((gr - row0) * K + chunk * 16);
+        }
+    }
+    // tile: first byte of this K step in the tile's first row; k_left = K - this step's k0.
+    __device__ __forceinline__ void issue(const uint8_t* tile, const uint8_t* lds, int wave, bool full_k,
+                                          int64_t k_left) const {
+        const uint32_t l0 = lds_addr(lds) + wave * 1024;
+        if (full_k) {
+#pragma unroll
+            for (int i = 0; i < kPerWave; ++i) copy_sv(tile, off[i], l0 + 4096 * i);
+        } else {
+            const bool in_k = chunk * 16 < k_left;
+            const uintptr_t zero = reinterpret_cast<uintptr_t>(g_zero16);
+#pragma unroll
+            for (int i = 0; i < kPerWave; ++i)
+                copy_v(in_k ? reinterpret_cast<uintptr_t>(tile + off[i]) : zero, l0 + 4096 * i);
         }
     }
 };
 
-// Map the linear block id to a (tile_m, tile_n) pair.  Consecutive block ids are dispatched to
-// the 8 XCDs in turn; the remap gives each XCD a contiguous range of the grouped tile order, and
-// the grouped order walks `group_m` tile rows before moving to the next tile column, so the blocks
+// LDS position of chunk c of row r: c ^ ((r >> 1) & 7).  ds_read_b128 is served 16 lanes (256
+// bytes, all 64 banks) at a time; a fragment read puts 16 consecutive rows at one chunk in those 16
+// lanes, and with this swizzle the 8 even rows fill one 128-byte half of the banks and the 8 odd
+// rows the other, without a conflict.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ ((row >> 1) & 7)) << 4); }
+
+// Scheduling order of one half-step: the kReads fragment reads of the next half go out one at a
+// time between the kMmas matrix-core instructions of the current half (which do not depend on
+// them), starting with matrix-core work, so LDS traffic is spread over the half-step and its
+// latency is hidden.
+template <int kReads, int kMmas>
+__device__ __forceinline__ void interleave_reads_with_mma() {
+    constexpr int kPer = kMmas / kReads > 0 ? kMmas / kReads : 1;
+#pragma unroll
+    for (int i = 0; i < kReads; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, kPer, 0);  // matrix-core instructions
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // then one LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kMmas - kPer * kReads > 0 ? kMmas - kPer * kReads : 0, 0);
+}
+
+// Map the linear block id to a (tile_m, tile_n) pair.  Consecutive block ids are dispatched to the
+// 8 XCDs in turn; the remap gives each XCD a contiguous range of the grouped tile order, and the
+// grouped order walks `group_m` tile rows before moving to the next tile column, so the blocks
 // sharing one XCD's L2 share operand tiles.
 __device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_m, int tiles_n, int group_m,
                                               int& tm, int& tn) {
@@ -79,149 +271,218 @@ __device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_m,
     tn = in / gm;
 }
 
-template <bool kFp8>
-struct Mfma;
-
-template <>
-struct Mfma<false> {
-    using Acc = v4i;
-    static constexpr int kKStep = 64;     // bytes of K per instruction
-    static constexpr int kChunks = 1;     // 16-byte chunks per lane per instruction
-    __device__ static __forceinline__ Acc zero() { return Acc{0, 0, 0, 0}; }
-    __device__ static __forceinline__ Acc run(const v4i (&a)[1], const v4i (&b)[1], Acc c) {
-        return __builtin_amdgcn_mfma_i32_16x16x64_i8(a[0], b[0], c, 0, 0, 0);
-    }
-    __device__ static __forceinline__ float to_float(int v) { return static_cast<float>(v); }
-};
-
-template <>
-struct Mfma<true> {
-    using Acc = v4f;
-    static constexpr int kKStep = 128;
-    static constexpr int kChunks = 2;
-    __device__ static __forceinline__ Acc zero() { return Acc{0.f, 0.f, 0.f, 0.f}; }
-    __device__ static __forceinline__ Acc run(const v4i (&a)[2], const v4i (&b)[2], Acc c) {
-        v8i a8 = {a[0][0], a[0][1], a[0][2], a[0][3], a[1][0], a[1][1], a[1][2], a[1][3]};
-        v8i b8 = {b[0][0], b[0][1], b[0][2], b[0][3], b[1][0], b[1][1], b[1][2], b[1][3]};
-        // format codes 0, 0: both operands OCP E4M3; scale operands 0 select the unscaled form.
-        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 0, 0, 0, 0, 0, 0);
-    }
-    __device__ static __forceinline__ float to_float(float v) { return v; }
-};
-
-// Dequantize and store four consecutive outputs of row m starting at column n.
-template <bool kFp8, bool kOutAcc, typename Acc>
-__device__ __forceinline__ void store4(const Acc& acc, int64_t m, int64_t n, int64_t M, int64_t N,
-                                       float sxm, const float* __restrict__ w_scale, uint16_t* __restrict__ y,
-                                       void* __restrict__ out_acc) {
-    if (m >= M) return;
-    if constexpr (kOutAcc) {
-        using T = typename std::remove_cv<typename std::remove_reference<decltype(acc[0])>::type>::type;
-        T* p = static_cast<T*>(out_acc) + m * N + n;
-        if (n + 3 < N && (N & 3) == 0) {
-            *reinterpret_cast<Acc*>(p) = acc;
-        } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (n + r < N) p[r] = acc[r];
-        }
-    } else {
-        uint32_t h[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float swn = (n + r < N) ? w_scale[n + r] : 0.0f;
-            h[r] = bf16_bits((Mfma<kFp8>::to_float(acc[r]) * sxm) * swn);
-        }
-        uint16_t* p = y + m * N + n;
-        if (n + 3 < N && (N & 3) == 0) {
-            *reinterpret_cast<uint2*>(p) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-        } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (n + r < N) p[r] = static_cast<uint16_t>(h[r]);
-        }
-    }
-}
-
-template <int kBM, int kBN, bool kFp8, bool kOutAcc>
-__global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(
+template <int kBM, int kBN, typename MM, bool kOutAcc>
+__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_tile_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ x_scale, const uint8_t* __restrict__ wq,
     const float* __restrict__ w_scale, int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y,
     void* __restrict__ out_acc, int tiles_m, int tiles_n, int group_m) {
-    using MF = Mfma<kFp8>;
-    using Acc = typename MF::Acc;
+    using Acc = typename MM::Acc;
     constexpr int kWM = kBM / 2, kWN = kBN / 2;
-    constexpr int kMT = kWM / 16, kNT = kWN / 16;
-    __shared__ __attribute__((aligned(16))) uint8_t lds_x[2][kBM * kBK];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_w[2][kBN * kBK];
+    constexpr int kMT = kWM / MM::kTile, kNT = kWN / MM::kTile;
+    constexpr int kC = MM::kChunks;
+    constexpr int kSub = 64 / MM::kKStep;            // instructions per 64-byte half-step
+    static_assert(kSub >= 1 && kSub * MM::kKStep == 64, "a half-step is 64 K bytes");
+    constexpr int kCopies = kBM / 32 + kBN / 32;     // copy instructions per wave per stage
+    // Three X stages, then three W stages; after the K loop the same LDS stages the bf16 output.
+    constexpr int kOutStride = kWN * 2 + 16;         // bytes per staged output row (padded)
+    static_assert(4 * kWM * kOutStride <= 3 * (kBM + kBN) * kBK, "output staging fits in the stages");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[3 * (kBM + kBN) * kBK];
+    uint8_t* const xs0 = smem;
+    uint8_t* const xs1 = smem + kBM * kBK;
+    uint8_t* const xs2 = smem + 2 * kBM * kBK;
+    uint8_t* const ws0 = smem + 3 * kBM * kBK;
+    uint8_t* const ws1 = ws0 + kBN * kBK;
+    uint8_t* const ws2 = ws0 + 2 * kBN * kBK;
 
     int tm, tn;
     tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
     const int64_t m0 = static_cast<int64_t>(tm) * kBM, n0 = static_cast<int64_t>(tn) * kBN;
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    // The wave index is uniform within a wave; readfirstlane lets the compiler keep it (and the
+    // LDS addresses of the copies, which must be scalar) in scalar registers.
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int lane = threadIdx.x % kWave;
     const int wm = wave >> 1, wn = wave & 1;
+    const int frag_row = lane % MM::kTile, frag_grp = lane / MM::kTile;
 
     Acc acc[kMT][kNT];
 #pragma unroll
     for (int i = 0; i < kMT; ++i)
 #pragma unroll
-        for (int j = 0; j < kNT; ++j) acc[i][j] = MF::zero();
+        for (int j = 0; j < kNT; ++j) acc[i][j] = MM::zero();
 
-    TileLoad<kBM> gx;
-    TileLoad<kBN> gw;
+    // Scales of this lane's outputs, requested before the K loop so they arrive during it.
+    constexpr int kG = MM::kGroups;
+    const int64_t mw0 = m0 + wm * kWM, nw0 = n0 + wn * kWN;
+    float sx_l[kMT];
+    v4f sw_l[kNT][kG];
+    if constexpr (!kOutAcc) {
+#pragma unroll
+        for (int i = 0; i < kMT; ++i) {
+            const int64_t m = mw0 + i * MM::kTile + out_row<MM::kTile>(lane);
+            sx_l[i] = m < M ? x_scale[m] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < kNT; ++j)
+#pragma unroll
+            for (int g = 0; g < kG; ++g) {
+                const int64_t n = nw0 + j * MM::kTile + out_col<MM::kTile>(lane, g);
+                if (n + 3 < N) {
+                    sw_l[j][g] = *reinterpret_cast<const v4f*>(w_scale + n);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sw_l[j][g][r] = (n + r < N) ? w_scale[n + r] : 0.0f;
+                }
+            }
+    }
+
     const int nk = static_cast<int>((K + kBK - 1) / kBK);
     const bool ragged_k = (K % kBK) != 0;
+    CopyPlan<kBM> cx;
+    CopyPlan<kBN> cw;
+    cx.init(m0, M, K, wave, lane);
+    cw.init(n0, N, K, wave, lane);
+    const uint8_t* xtile = xq + m0 * K;
+    const uint8_t* wtile = wq + n0 * K;
+    auto issue = [&](int kt, const uint8_t* lx, const uint8_t* lw) {
+        const int64_t k0 = static_cast<int64_t>(kt) * kBK;
+        const bool full = !(ragged_k && kt == nk - 1);
+        cx.issue(xtile + k0, lx, wave, full, K - k0);
+        cw.issue(wtile + k0, lw, wave, full, K - k0);
+    };
+    auto issue_full = [&](int kt, const uint8_t* lx, const uint8_t* lw) {   // kt < n_plain
+        const int64_t k0 = static_cast<int64_t>(kt) * kBK;
+        cx.issue(xtile + k0, lx, wave, true, 0);
+        cw.issue(wtile + k0, lw, wave, true, 0);
+    };
 
-    gx.load(xq, m0, M, K, 0, !(ragged_k && nk == 1));
-    gw.load(wq, n0, N, K, 0, !(ragged_k && nk == 1));
-    gx.store(lds_x[0]);
-    gw.store(lds_w[0]);
-    __syncthreads();
-
-    const int frag_row = lane & 15, frag_grp = lane >> 4;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            const bool full = !(ragged_k && kt + 2 == nk);
-            gx.load(xq, m0, M, K, static_cast<int64_t>(kt + 1) * kBK, full);
-            gw.load(wq, n0, N, K, static_cast<int64_t>(kt + 1) * kBK, full);
-        }
-        const uint8_t* lx = lds_x[cur];
-        const uint8_t* lw = lds_w[cur];
+    struct Frags {
+        v4i x[kSub][kMT][kC];
+        v4i w[kSub][kNT][kC];
+    };
+    auto read = [&](Frags& f, const uint8_t* lx, const uint8_t* lw, int half) {
 #pragma unroll
-        for (int ks = 0; ks < kBK / MF::kKStep; ++ks) {
-            v4i fx[kMT][MF::kChunks], fw[kNT][MF::kChunks];
+        for (int s = 0; s < kSub; ++s)
 #pragma unroll
-            for (int c = 0; c < MF::kChunks; ++c) {
-                const int chunk = ks * (MF::kKStep / 16) + frag_grp * MF::kChunks + c;
+            for (int c = 0; c < kC; ++c) {
+                const int chunk = half * 4 + s * (MM::kKStep / 16) + frag_grp * kC + c;
 #pragma unroll
                 for (int i = 0; i < kMT; ++i)
-                    fx[i][c] = *reinterpret_cast<const v4i*>(lx + swz(wm * kWM + i * 16 + frag_row, chunk));
+                    f.x[s][i][c] =
+                        *reinterpret_cast<const v4i*>(lx + swz(wm * kWM + i * MM::kTile + frag_row, chunk));
 #pragma unroll
                 for (int j = 0; j < kNT; ++j)
-                    fw[j][c] = *reinterpret_cast<const v4i*>(lw + swz(wn * kWN + j * 16 + frag_row, chunk));
+                    f.w[s][j][c] =
+                        *reinterpret_cast<const v4i*>(lw + swz(wn * kWN + j * MM::kTile + frag_row, chunk));
             }
+    };
+    auto mma = [&](const Frags& f) {
+#pragma unroll
+        for (int s = 0; s < kSub; ++s)
 #pragma unroll
             for (int i = 0; i < kMT; ++i)
 #pragma unroll
-                for (int j = 0; j < kNT; ++j) acc[i][j] = MF::run(fw[j], fx[i], acc[i][j]);
+                for (int j = 0; j < kNT; ++j) acc[i][j] = MM::run(f.w[s][j], f.x[s][i], acc[i][j]);
+    };
+
+    Frags f0, f1;
+    constexpr int kReads = (kMT + kNT) * kC * kSub, kMmas = kMT * kNT * kSub;
+    // One K step on stage (lx, lw) whose first-half fragments are already in f0; the next stage is
+    // (nx, nw), and the stage of step kt receives K step kt + 3 once everyone has read it.
+    // full_step is the same for kt + 3 < nk, without branches: inside the steady-state loop the
+    // compiler then sees straight-line code and waits only for the fragments each half needs.
+    auto full_step = [&](int kt, const uint8_t* lx, const uint8_t* lw, const uint8_t* nx, const uint8_t* nw) {
+        read(f1, lx, lw, 1);
+        mma(f0);
+        interleave_reads_with_mma<kReads, kMmas>();
+        wait_lds_reads();
+        wait_copies<kCopies>();
+        block_barrier();
+        issue_full(kt + 3, lx, lw);
+        read(f0, nx, nw, 0);
+        mma(f1);
+        interleave_reads_with_mma<kReads, kMmas>();
+    };
+    auto step = [&](int kt, const uint8_t* lx, const uint8_t* lw, const uint8_t* nx, const uint8_t* nw) {
+        read(f1, lx, lw, 1);
+        mma(f0);
+        wait_lds_reads();
+        if (kt + 1 < nk) {
+            if (kt + 2 < nk) wait_copies<kCopies>();
+            else wait_copies<0>();
+            block_barrier();
+            if (kt + 3 < nk) issue(kt + 3, lx, lw);
+            read(f0, nx, nw, 0);
         }
-        if (more) {
-            gx.store(lds_x[cur ^ 1]);
-            gw.store(lds_w[cur ^ 1]);
-        }
-        __syncthreads();
+        mma(f1);
+    };
+
+    issue(0, xs0, ws0);
+    if (nk > 1) issue(1, xs1, ws1);
+    if (nk > 2) issue(2, xs2, ws2);
+    if (nk > 2) wait_copies<2 * kCopies>();
+    else if (nk > 1) wait_copies<kCopies>();
+    else wait_copies<0>();
+    block_barrier();
+    read(f0, xs0, ws0, 0);
+    // K steps that need no zero fill: all of them, or all but a ragged last one.
+    const int n_plain = ragged_k ? nk - 1 : nk;
+    int kt = 0;
+    for (; kt + 5 < n_plain; kt += 3) {      // steps kt .. kt + 2 copy plain K steps kt + 3 .. kt + 5
+        full_step(kt, xs0, ws0, xs1, ws1);
+        full_step(kt + 1, xs1, ws1, xs2, ws2);
+        full_step(kt + 2, xs2, ws2, xs0, ws0);
+    }
+    for (; kt < nk; kt += 3) {               // the last (at most five) steps
+        step(kt, xs0, ws0, xs1, ws1);
+        if (kt + 1 < nk) step(kt + 1, xs1, ws1, xs2, ws2);
+        if (kt + 2 < nk) step(kt + 2, xs2, ws2, xs0, ws0);
     }
 
+    if constexpr (kOutAcc) {
 #pragma unroll
-    for (int i = 0; i < kMT; ++i) {
-        const int64_t m = m0 + wm * kWM + i * 16 + frag_row;
-        const float sxm = (!kOutAcc && m < M) ? x_scale[m] : 0.0f;
+        for (int i = 0; i < kMT; ++i)
 #pragma unroll
-        for (int j = 0; j < kNT; ++j) {
-            const int64_t n = n0 + wn * kWN + j * 16 + frag_grp * 4;
-            store4<kFp8, kOutAcc>(acc[i][j], m, n, M, N, sxm, w_scale, y, out_acc);
+            for (int j = 0; j < kNT; ++j)
+                store_block<MM, kOutAcc>(acc[i][j], mw0 + i * MM::kTile, nw0 + j * MM::kTile, lane, M, N, x_scale,
+                                         w_scale, y, out_acc);
+    } else {
+        // Dequantize in registers, stage the wave's kWM x kWN bf16 tile in LDS (rows padded to
+        // kOutStride bytes), and write it back as 16-byte pieces of whole output rows.
+        block_barrier();                 // every wave has finished reading the stages
+        uint8_t* const ot = smem + wave * (kWM * kOutStride);
+#pragma unroll
+        for (int i = 0; i < kMT; ++i)
+#pragma unroll
+            for (int j = 0; j < kNT; ++j)
+#pragma unroll
+                for (int g = 0; g < kG; ++g) {
+                    uint32_t h[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        h[r] = bf16_bits((static_cast<float>(acc[i][j][4 * g + r]) * sx_l[i]) * sw_l[j][g][r]);
+                    const int row = i * MM::kTile + out_row<MM::kTile>(lane);
+                    const int col = j * MM::kTile + out_col<MM::kTile>(lane, g);
+                    *reinterpret_cast<uint2*>(ot + row * kOutStride + col * 2) =
+                        make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                }
+        wait_lds_reads();                // this wave's LDS writes are complete before it reads them
+        constexpr int kPieces = kWM * kWN * 2 / 16;  // 16-byte pieces in the wave's tile
+        const bool vec_ok = (N % 8) == 0;
+#pragma unroll
+        for (int p = lane; p < kPieces; p += kWave) {
+            const int row = p / (kWN / 8), c = p % (kWN / 8);
+            const int64_t m = mw0 + row, n = nw0 + c * 8;
+            const uint4 v = *reinterpret_cast<const uint4*>(ot + row * kOutStride + c * 16);
+            if (m >= M) continue;
+            uint16_t* dst = y + m * N + n;
+            if (vec_ok && n + 7 < N) {
+                *reinterpret_cast<uint4*>(dst) = v;
+            } else {
+                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (n + e < N) dst[e] = static_cast<uint16_t>(w4[e / 2] >> (16 * (e % 2)));
+            }
         }
     }
 }
@@ -232,13 +493,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(
 // from global memory (X is small and stays in cache), and the 4 partial sums are added in LDS at
 // the end (exact for INT8).  N / 16 blocks keep every CU streaming.
 // ------------------------------------------------------------------------------------------------
-template <int kMT, bool kFp8, bool kOutAcc>
+template <int kMT, typename MM, bool kOutAcc>
 __global__ __launch_bounds__(kThreads) void gemm_small_m_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ x_scale, const uint8_t* __restrict__ wq,
     const float* __restrict__ w_scale, int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y,
     void* __restrict__ out_acc) {
-    using MF = Mfma<kFp8>;
-    using Acc = typename MF::Acc;
+    using Acc = typename MM::Acc;
+    static_assert(MM::kTile == 16, "16x16 blocks");
     __shared__ Acc red[3][kMT][kWave];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
@@ -255,14 +516,14 @@ __global__ __launch_bounds__(kThreads) void gemm_small_m_kernel(
     }
     Acc acc[kMT];
 #pragma unroll
-    for (int i = 0; i < kMT; ++i) acc[i] = MF::zero();
+    for (int i = 0; i < kMT; ++i) acc[i] = MM::zero();
 
-    const int64_t nsteps = (K + MF::kKStep - 1) / MF::kKStep;
+    const int64_t nsteps = (K + MM::kKStep - 1) / MM::kKStep;
     for (int64_t st = wave; st < nsteps; st += 4) {
-        v4i fw[MF::kChunks], fx[kMT][MF::kChunks];
+        v4i fw[MM::kChunks], fx[kMT][MM::kChunks];
 #pragma unroll
-        for (int c = 0; c < MF::kChunks; ++c) {
-            const int64_t k = st * MF::kKStep + (frag_grp * MF::kChunks + c) * 16;
+        for (int c = 0; c < MM::kChunks; ++c) {
+            const int64_t k = st * MM::kKStep + (frag_grp * MM::kChunks + c) * 16;
             const bool ok = k < K;
             fw[c] = ok ? *reinterpret_cast<const v4i*>(wrow + k) : v4i{0, 0, 0, 0};
 #pragma unroll
@@ -270,7 +531,7 @@ __global__ __launch_bounds__(kThreads) void gemm_small_m_kernel(
                 fx[i][c] = ok ? *reinterpret_cast<const v4i*>(xrow[i] + k) : v4i{0, 0, 0, 0};
         }
 #pragma unroll
-        for (int i = 0; i < kMT; ++i) acc[i] = MF::run(fw, fx[i], acc[i]);
+        for (int i = 0; i < kMT; ++i) acc[i] = MM::run(fw, fx[i], acc[i]);
     }
     if (wave > 0) {
 #pragma unroll
@@ -283,26 +544,24 @@ __global__ __launch_bounds__(kThreads) void gemm_small_m_kernel(
             Acc a = acc[i];
 #pragma unroll
             for (int w = 0; w < 3; ++w) a += red[w][i][lane];
-            const int64_t m = static_cast<int64_t>(i) * 16 + frag_row;
-            const float sxm = (!kOutAcc && m < M) ? x_scale[m] : 0.0f;
-            store4<kFp8, kOutAcc>(a, m, n0 + frag_grp * 4, M, N, sxm, w_scale, y, out_acc);
+            store_block<MM, kOutAcc>(a, static_cast<int64_t>(i) * 16, n0, lane, M, N, x_scale, w_scale, y, out_acc);
         }
     }
 }
 
-template <bool kFp8, bool kOutAcc>
+template <typename M16, typename MT, bool kOutAcc>
 hipError_t gemm_dispatch(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale,
                          int64_t M, int64_t N, int64_t K, uint16_t* y, void* out_acc, hipStream_t st) {
     if (M <= 64) {
         dim3 grid(static_cast<unsigned>((N + 15) / 16));
         if (M <= 16)
-            hipLaunchKernelGGL((gemm_small_m_kernel<1, kFp8, kOutAcc>), grid, dim3(kThreads), 0, st, xq, x_scale, wq,
+            hipLaunchKernelGGL((gemm_small_m_kernel<1, M16, kOutAcc>), grid, dim3(kThreads), 0, st, xq, x_scale, wq,
                                w_scale, M, N, K, y, out_acc);
         else if (M <= 32)
-            hipLaunchKernelGGL((gemm_small_m_kernel<2, kFp8, kOutAcc>), grid, dim3(kThreads), 0, st, xq, x_scale, wq,
+            hipLaunchKernelGGL((gemm_small_m_kernel<2, M16, kOutAcc>), grid, dim3(kThreads), 0, st, xq, x_scale, wq,
                                w_scale, M, N, K, y, out_acc);
         else
-            hipLaunchKernelGGL((gemm_small_m_kernel<4, kFp8, kOutAcc>), grid, dim3(kThreads), 0, st, xq, x_scale, wq,
+            hipLaunchKernelGGL((gemm_small_m_kernel<4, M16, kOutAcc>), grid, dim3(kThreads), 0, st, xq, x_scale, wq,
                                w_scale, M, N, K, y, out_acc);
         return hipGetLastError();
     }
@@ -310,7 +569,7 @@ hipError_t gemm_dispatch(const uint8_t* xq, const float* x_scale, const uint8_t*
     const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
     const int tiles_n = static_cast<int>((N + kBN - 1) / kBN);
     const int group_m = 4;
-    hipLaunchKernelGGL((gemm_tile_kernel<kBM, kBN, kFp8, kOutAcc>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((gemm_tile_kernel<kBM, kBN, MT, kOutAcc>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, st,
                        xq, x_scale, wq, w_scale, M, N, K, y, out_acc, tiles_m, tiles_n, group_m);
     return hipGetLastError();
 }
@@ -321,11 +580,11 @@ hipError_t launch_gemm(const uint8_t* xq, const float* x_scale, const uint8_t* w
                        int64_t M, int64_t N, int64_t K, uint16_t* y, void* out_acc, hipStream_t st) {
     if (M <= 0 || N <= 0) return hipSuccess;
     if (out_acc) {
-        if (fp8) return gemm_dispatch<true, true>(xq, nullptr, wq, nullptr, M, N, K, nullptr, out_acc, st);
-        return gemm_dispatch<false, true>(xq, nullptr, wq, nullptr, M, N, K, nullptr, out_acc, st);
+        if (fp8) return gemm_dispatch<MmaF8x16, MmaF8x32, true>(xq, nullptr, wq, nullptr, M, N, K, nullptr, out_acc, st);
+        return gemm_dispatch<MmaI8x16, MmaI8x32, true>(xq, nullptr, wq, nullptr, M, N, K, nullptr, out_acc, st);
     }
-    if (fp8) return gemm_dispatch<true, false>(xq, x_scale, wq, w_scale, M, N, K, y, nullptr, st);
-    return gemm_dispatch<false, false>(xq, x_scale, wq, w_scale, M, N, K, y, nullptr, st);
+    if (fp8) return gemm_dispatch<MmaF8x16, MmaF8x32, false>(xq, x_scale, wq, w_scale, M, N, K, y, nullptr, st);
+    return gemm_dispatch<MmaI8x16, MmaI8x32, false>(xq, x_scale, wq, w_scale, M, N, K, y, nullptr, st);
 }
 
 }  // namespace w8a8
