@@ -90,10 +90,12 @@ __device__ __forceinline__ uint32_t code_of(float xs, float scale) {
 template <bool kFp8>
 __device__ __forceinline__ constexpr float qmax() { return kFp8 ? 448.0f : 127.0f; }
 
-// bf16 round to nearest even of a finite float.
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// Two finite floats rounded to bf16 (nearest, ties to even) and packed, a in the low half:
+// one v_cvt_pk_bf16_f32 on gfx950.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
 }
 
 }  // namespace w8a8

@@ -103,19 +103,22 @@ __device__ __forceinline__ void store4(const T (&a)[4], int64_t m, int64_t n, in
                 if (n + r < N) p[r] = a[r];
         }
     } else {
-        uint32_t h[4];
+        float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float swn = (n + r < N) ? w_scale[n + r] : 0.0f;
-            h[r] = bf16_bits((static_cast<float>(a[r]) * sxm) * swn);
+            v[r] = (static_cast<float>(a[r]) * sxm) * swn;
         }
+        const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
         uint16_t* p = y + m * N + n;
         if (n + 3 < N && (N & 3) == 0) {
-            *reinterpret_cast<uint2*>(p) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
         } else {
+            const uint16_t h[4] = {static_cast<uint16_t>(lo), static_cast<uint16_t>(lo >> 16),
+                                   static_cast<uint16_t>(hi), static_cast<uint16_t>(hi >> 16)};
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                if (n + r < N) p[r] = static_cast<uint16_t>(h[r]);
+                if (n + r < N) p[r] = h[r];
         }
     }
 }
@@ -216,19 +219,16 @@ struct CopyPlan {
             off[i] = static_cast<uint32_t>((gr - row0) * K + chunk * 16);
         }
     }
-    // tile: first byte of this K step in the tile's first row; k_left = K - this step's k0.
-    __device__ __forceinline__ void issue(const uint8_t* tile, const uint8_t* lds, int wave, bool full_k,
-                                          int64_t k_left) const {
-        const uint32_t l0 = lds_addr(lds) + wave * 1024;
+    // Copy i of a K step.  tile: first byte of the K step in the tile's first row; k_left: K minus
+    // the K step's first byte (only looked at when !full_k).
+    __device__ __forceinline__ void one(int i, const uint8_t* tile, const uint8_t* lds, int wave, bool full_k,
+                                        int64_t k_left) const {
+        const uint32_t l = lds_addr(lds) + wave * 1024 + 4096 * i;
         if (full_k) {
-#pragma unroll
-            for (int i = 0; i < kPerWave; ++i) copy_sv(tile, off[i], l0 + 4096 * i);
+            copy_sv(tile, off[i], l);
         } else {
             const bool in_k = chunk * 16 < k_left;
-            const uintptr_t zero = reinterpret_cast<uintptr_t>(g_zero16);
-#pragma unroll
-            for (int i = 0; i < kPerWave; ++i)
-                copy_v(in_k ? reinterpret_cast<uintptr_t>(tile + off[i]) : zero, l0 + 4096 * i);
+            copy_v(in_k ? reinterpret_cast<uintptr_t>(tile + off[i]) : reinterpret_cast<uintptr_t>(g_zero16), l);
         }
     }
 };
@@ -238,21 +238,6 @@ struct CopyPlan {
 // lanes, and with this swizzle the 8 even rows fill one 128-byte half of the banks and the 8 odd
 // rows the other, without a conflict.
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ ((row >> 1) & 7)) << 4); }
-
-// Scheduling order of one half-step: the kReads fragment reads of the next half go out one at a
-// time between the kMmas matrix-core instructions of the current half (which do not depend on
-// them), starting with matrix-core work, so LDS traffic is spread over the half-step and its
-// latency is hidden.
-template <int kReads, int kMmas>
-__device__ __forceinline__ void interleave_reads_with_mma() {
-    constexpr int kPer = kMmas / kReads > 0 ? kMmas / kReads : 1;
-#pragma unroll
-    for (int i = 0; i < kReads; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, kPer, 0);  // matrix-core instructions
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // then one LDS read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, kMmas - kPer * kReads > 0 ? kMmas - kPer * kReads : 0, 0);
-}
 
 // Map the linear block id to a (tile_m, tile_n) pair.  Consecutive block ids are dispatched to the
 // 8 XCDs in turn; the remap gives each XCD a contiguous range of the grouped tile order, and the
@@ -343,100 +328,114 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     cw.init(n0, N, K, wave, lane);
     const uint8_t* xtile = xq + m0 * K;
     const uint8_t* wtile = wq + n0 * K;
-    auto issue = [&](int kt, const uint8_t* lx, const uint8_t* lw) {
+    auto stage_x = [&](int kt) { return kt % 3 == 0 ? xs0 : (kt % 3 == 1 ? xs1 : xs2); };
+    auto stage_w = [&](int kt) { return kt % 3 == 0 ? ws0 : (kt % 3 == 1 ? ws1 : ws2); };
+    // Copy c (0 <= c < kCopies) of K step kt: the X copies first, then the W copies.  A stage's
+    // copies go out in two parts, A = [0, kCopies / 2) and B = [kCopies / 2, kCopies).
+    constexpr int kPartA = kCopies / 2;
+    auto copy = [&](int c, int kt, const uint8_t* lx, const uint8_t* lw, bool plain) {
         const int64_t k0 = static_cast<int64_t>(kt) * kBK;
-        const bool full = !(ragged_k && kt == nk - 1);
-        cx.issue(xtile + k0, lx, wave, full, K - k0);
-        cw.issue(wtile + k0, lw, wave, full, K - k0);
+        if (c < CopyPlan<kBM>::kPerWave) cx.one(c, xtile + k0, lx, wave, plain, K - k0);
+        else cw.one(c - CopyPlan<kBM>::kPerWave, wtile + k0, lw, wave, plain, K - k0);
     };
-    auto issue_full = [&](int kt, const uint8_t* lx, const uint8_t* lw) {   // kt < n_plain
-        const int64_t k0 = static_cast<int64_t>(kt) * kBK;
-        cx.issue(xtile + k0, lx, wave, true, 0);
-        cw.issue(wtile + k0, lw, wave, true, 0);
+    auto copies = [&](int c0, int c1, int kt) {      // part of K step kt, any kt < nk
+        const bool plain = !(ragged_k && kt == nk - 1);
+        for (int c = c0; c < c1; ++c) copy(c, kt, stage_x(kt), stage_w(kt), plain);
     };
 
     struct Frags {
         v4i x[kSub][kMT][kC];
         v4i w[kSub][kNT][kC];
     };
-    auto read = [&](Frags& f, const uint8_t* lx, const uint8_t* lw, int half) {
-#pragma unroll
-        for (int s = 0; s < kSub; ++s)
-#pragma unroll
-            for (int c = 0; c < kC; ++c) {
-                const int chunk = half * 4 + s * (MM::kKStep / 16) + frag_grp * kC + c;
-#pragma unroll
-                for (int i = 0; i < kMT; ++i)
-                    f.x[s][i][c] =
-                        *reinterpret_cast<const v4i*>(lx + swz(wm * kWM + i * MM::kTile + frag_row, chunk));
-#pragma unroll
-                for (int j = 0; j < kNT; ++j)
-                    f.w[s][j][c] =
-                        *reinterpret_cast<const v4i*>(lw + swz(wn * kWN + j * MM::kTile + frag_row, chunk));
-            }
+    // Fragment read r of a half-step (s outer, then chunk, then the X tiles and the W tiles).
+    auto read_one = [&](Frags& f, const uint8_t* lx, const uint8_t* lw, int half, int r) {
+        constexpr int kPerSC = kMT + kNT;
+        const int s = r / (kC * kPerSC), rem = r % (kC * kPerSC);
+        const int c = rem / kPerSC, tt = rem % kPerSC;
+        const int chunk = half * 4 + s * (MM::kKStep / 16) + frag_grp * kC + c;
+        if (tt < kMT)
+            f.x[s][tt][c] = *reinterpret_cast<const v4i*>(lx + swz(wm * kWM + tt * MM::kTile + frag_row, chunk));
+        else
+            f.w[s][tt - kMT][c] =
+                *reinterpret_cast<const v4i*>(lw + swz(wn * kWN + (tt - kMT) * MM::kTile + frag_row, chunk));
     };
-    auto mma = [&](const Frags& f) {
+    auto mma_one = [&](const Frags& f, int q) {
+        const int s = q / (kMT * kNT), i = (q / kNT) % kMT, j = q % kNT;
+        acc[i][j] = MM::run(f.w[s][j], f.x[s][i], acc[i][j]);
+    };
+    constexpr int kReads = (kMT + kNT) * kC * kSub, kMmas = kMT * kNT * kSub;
+
+    // One half-step of the steady state, in a fixed order: slot q issues matrix-core instruction q
+    // of the current fragments, the fragment reads of the next half assigned to slot q, and the
+    // copies assigned to slot q (copies [c0, c0 + kPartA) of K step ckt, which is plain).
+    auto half_step = [&](const Frags& cur, Frags& nxt, const uint8_t* lx, const uint8_t* lw, int half, int c0,
+                         int ckt, const uint8_t* cxl, const uint8_t* cwl) {
+        const int64_t k0 = static_cast<int64_t>(ckt) * kBK;
 #pragma unroll
-        for (int s = 0; s < kSub; ++s)
+        for (int q = 0; q < kMmas; ++q) {
+            mma_one(cur, q);
 #pragma unroll
-            for (int i = 0; i < kMT; ++i)
+            for (int r = 0; r < kReads; ++r)
+                if (r * kMmas / kReads == q) read_one(nxt, lx, lw, half, r);
 #pragma unroll
-                for (int j = 0; j < kNT; ++j) acc[i][j] = MM::run(f.w[s][j], f.x[s][i], acc[i][j]);
+            for (int c = 0; c < kPartA; ++c)
+                if (c * kMmas / kPartA == q) {
+                    const int cc = c0 + c;
+                    if (cc < CopyPlan<kBM>::kPerWave) cx.one(cc, xtile + k0, cxl, wave, true, 0);
+                    else cw.one(cc - CopyPlan<kBM>::kPerWave, wtile + k0, cwl, wave, true, 0);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
     Frags f0, f1;
-    constexpr int kReads = (kMT + kNT) * kC * kSub, kMmas = kMT * kNT * kSub;
-    // One K step on stage (lx, lw) whose first-half fragments are already in f0; the next stage is
-    // (nx, nw), and the stage of step kt receives K step kt + 3 once everyone has read it.
-    // full_step is the same for kt + 3 < nk, without branches: inside the steady-state loop the
-    // compiler then sees straight-line code and waits only for the fragments each half needs.
-    auto full_step = [&](int kt, const uint8_t* lx, const uint8_t* lw, const uint8_t* nx, const uint8_t* nw) {
-        read(f1, lx, lw, 1);
-        mma(f0);
-        interleave_reads_with_mma<kReads, kMmas>();
+    // Steady-state K step kt (all copies plain and in range): the first half multiplies f0 (half 0
+    // of stage kt) while reading f1 (half 1) and sending copies B of K step kt + 2; then the stage
+    // of kt + 1 is waited for and the block meets; the second half multiplies f1 while reading f0
+    // (half 0 of stage kt + 1) and sending copies A of K step kt + 3 into the stage just read.
+    // Stages: (lx, lw) of kt, (nx, nw) of kt + 1, (bx, bw) of kt + 2; kt + 3 reuses (lx, lw).
+    auto full_step = [&](int kt, const uint8_t* lx, const uint8_t* lw, const uint8_t* nx, const uint8_t* nw,
+                         const uint8_t* bx, const uint8_t* bw) {
+        half_step(f0, f1, lx, lw, 1, kPartA, kt + 2, bx, bw);
         wait_lds_reads();
         wait_copies<kCopies>();
         block_barrier();
-        issue_full(kt + 3, lx, lw);
-        read(f0, nx, nw, 0);
-        mma(f1);
-        interleave_reads_with_mma<kReads, kMmas>();
+        half_step(f1, f0, nx, nw, 0, 0, kt + 3, lx, lw);
     };
-    auto step = [&](int kt, const uint8_t* lx, const uint8_t* lw, const uint8_t* nx, const uint8_t* nw) {
-        read(f1, lx, lw, 1);
-        mma(f0);
+    // The same protocol for any kt, with the copies and the next stage guarded.
+    auto step = [&](int kt) {
+        for (int r = 0; r < kReads; ++r) read_one(f1, stage_x(kt), stage_w(kt), 1, r);
+        for (int q = 0; q < kMmas; ++q) mma_one(f0, q);
+        if (kt + 2 < nk) copies(kPartA, kCopies, kt + 2);
         wait_lds_reads();
         if (kt + 1 < nk) {
             if (kt + 2 < nk) wait_copies<kCopies>();
             else wait_copies<0>();
             block_barrier();
-            if (kt + 3 < nk) issue(kt + 3, lx, lw);
-            read(f0, nx, nw, 0);
+            if (kt + 3 < nk) copies(0, kPartA, kt + 3);
+            for (int r = 0; r < kReads; ++r) read_one(f0, stage_x(kt + 1), stage_w(kt + 1), 0, r);
         }
-        mma(f1);
+        for (int q = 0; q < kMmas; ++q) mma_one(f1, q);
     };
 
-    issue(0, xs0, ws0);
-    if (nk > 1) issue(1, xs1, ws1);
-    if (nk > 2) issue(2, xs2, ws2);
-    if (nk > 2) wait_copies<2 * kCopies>();
+    // Prologue: K steps 0 and 1 whole and part A of K step 2; wait for step 0.
+    copies(0, kCopies, 0);
+    if (nk > 1) copies(0, kCopies, 1);
+    if (nk > 2) copies(0, kPartA, 2);
+    if (nk > 2) wait_copies<kCopies + kPartA>();
     else if (nk > 1) wait_copies<kCopies>();
     else wait_copies<0>();
     block_barrier();
-    read(f0, xs0, ws0, 0);
+    for (int r = 0; r < kReads; ++r) read_one(f0, xs0, ws0, 0, r);
     // K steps that need no zero fill: all of them, or all but a ragged last one.
     const int n_plain = ragged_k ? nk - 1 : nk;
     int kt = 0;
-    for (; kt + 5 < n_plain; kt += 3) {      // steps kt .. kt + 2 copy plain K steps kt + 3 .. kt + 5
-        full_step(kt, xs0, ws0, xs1, ws1);
-        full_step(kt + 1, xs1, ws1, xs2, ws2);
-        full_step(kt + 2, xs2, ws2, xs0, ws0);
+    for (; kt + 5 < n_plain; kt += 3) {      // steps kt .. kt + 2 copy plain K steps up to kt + 5
+        full_step(kt, xs0, ws0, xs1, ws1, xs2, ws2);
+        full_step(kt + 1, xs1, ws1, xs2, ws2, xs0, ws0);
+        full_step(kt + 2, xs2, ws2, xs0, ws0, xs1, ws1);
     }
-    for (; kt < nk; kt += 3) {               // the last (at most five) steps
-        step(kt, xs0, ws0, xs1, ws1);
-        if (kt + 1 < nk) step(kt + 1, xs1, ws1, xs2, ws2);
-        if (kt + 2 < nk) step(kt + 2, xs2, ws2, xs0, ws0);
-    }
+    for (; kt < nk; ++kt) step(kt);          // the last (at most five) steps
 
     if constexpr (kOutAcc) {
 #pragma unroll
@@ -456,14 +455,14 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
             for (int j = 0; j < kNT; ++j)
 #pragma unroll
                 for (int g = 0; g < kG; ++g) {
-                    uint32_t h[4];
+                    float v[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        h[r] = bf16_bits((static_cast<float>(acc[i][j][4 * g + r]) * sx_l[i]) * sw_l[j][g][r]);
+                        v[r] = (static_cast<float>(acc[i][j][4 * g + r]) * sx_l[i]) * sw_l[j][g][r];
                     const int row = i * MM::kTile + out_row<MM::kTile>(lane);
                     const int col = j * MM::kTile + out_col<MM::kTile>(lane, g);
                     *reinterpret_cast<uint2*>(ot + row * kOutStride + col * 2) =
-                        make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                 }
         wait_lds_reads();                // this wave's LDS writes are complete before it reads them
         constexpr int kPieces = kWM * kWN * 2 / 16;  // 16-byte pieces in the wave's tile
