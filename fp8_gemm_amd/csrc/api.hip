@@ -45,10 +45,14 @@ W8A8_API w8a8_status w8a8_smooth_scales(const void* x, w8a8_dtype x_dtype, int64
     if (!accumulate) e = w8a8::launch_fill(ax, K, 0.0f, stream);
     if (e == hipSuccess) e = w8a8::launch_absmax_cols(x, x_dtype == W8A8_BF16, M, K, nullptr, ax, stream);
     if (e == hipSuccess) {
-        if (N > 0) e = w8a8::launch_absmax_rows(w, w_dtype == W8A8_BF16, K, N, aw, stream);
-        else e = w8a8::launch_fill(aw, K, 0.0f, stream);
+        if (N > 0) {
+            // row maxima of W and, fused, the smoothing factors from the finished ax
+            e = w8a8::launch_absmax_rows(w, w_dtype == W8A8_BF16, K, N, aw, ax, alpha, s, stream);
+        } else {
+            e = w8a8::launch_fill(aw, K, 0.0f, stream);
+            if (e == hipSuccess) e = w8a8::launch_smooth_factors(ax, aw, K, alpha, s, stream);
+        }
     }
-    if (e == hipSuccess) e = w8a8::launch_smooth_factors(ax, aw, K, alpha, s, stream);
     return from_hip(e);
 }
 

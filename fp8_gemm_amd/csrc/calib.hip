@@ -25,8 +25,10 @@ __device__ __forceinline__ float load1(const void* base, int64_t i) {
     else return static_cast<const float*>(base)[i];
 }
 
-// 8 elements starting at column c of a row; columns >= C read as 0.  kVec: the row is 16-byte
-// aligned and C is a multiple of 8, so a chunk is entirely inside or outside the row.
+// 8 elements starting at column c of a row, c < C.  kVec: the row is 16-byte aligned and C is a
+// multiple of 8, so the chunk is inside the row; otherwise columns past C re-read column C - 1
+// (harmless for a maximum).  Loads are unconditional so that a wave's loads are all in flight
+// together.
 template <bool kBf16, bool kVec>
 __device__ __forceinline__ void load_chunk(const void* base, int64_t row_start, int64_t c, int64_t C,
                                            float (&v)[8]) {
@@ -34,33 +36,40 @@ __device__ __forceinline__ void load_chunk(const void* base, int64_t row_start, 
         load8<kBf16>(base, row_start + c, v);
     } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (c + e < C) ? load1<kBf16>(base, row_start + c + e) : 0.0f;
+        for (int e = 0; e < 8; ++e) v[e] = load1<kBf16>(base, row_start + (c + e < C ? c + e : C - 1));
     }
 }
 
 // Column maxima of |a[r, c] * row_scale[r]| over a block of kRowsPerBlock rows and 512 columns,
-// merged across waves in LDS and across blocks with an atomic maximum.
-template <bool kBf16, bool kVec>
+// merged across waves in LDS and across blocks with an atomic maximum.  Rows past R re-read row
+// R - 1 and columns past C re-read the last chunk: duplicates do not change a maximum.
+template <bool kBf16, bool kVec, bool kScaled>
 __global__ __launch_bounds__(256) void absmax_cols_kernel(const void* __restrict__ a, int64_t R, int64_t C,
                                                           const float* __restrict__ row_scale,
                                                           float* __restrict__ out) {
     __shared__ float part[4][kColsPerWave];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int64_t c = static_cast<int64_t>(blockIdx.x) * kColsPerWave + lane * 8;
+    const int64_t cl = c < C ? c : (kVec ? C - 8 : C - 1);
     const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kRowsPerBlock;
+    constexpr int kRows = kRowsPerBlock / 4;
+    float v[kRows][8];
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+        int64_t r = r0 + wave + 4 * i;
+        r = r < R ? r : R - 1;
+        load_chunk<kBf16, kVec>(a, r * C, cl, C, v[i]);
+    }
     float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (c < C) {
 #pragma unroll
-        for (int i = 0; i < kRowsPerBlock / 4; ++i) {
+    for (int i = 0; i < kRows; ++i) {
+        float rs = 1.0f;
+        if constexpr (kScaled) {
             const int64_t r = r0 + wave + 4 * i;
-            if (r < R) {
-                float v[8];
-                load_chunk<kBf16, kVec>(a, r * C, c, C, v);
-                const float rs = row_scale ? row_scale[r] : 1.0f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) m[e] = fmaxf(m[e], fabsf(row_scale ? rs * v[e] : v[e]));
-            }
+            rs = row_scale[r < R ? r : R - 1];
         }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m[e] = fmaxf(m[e], fabsf(kScaled ? rs * v[i][e] : v[i][e]));
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) part[wave][lane * 8 + e] = m[e];
@@ -68,45 +77,69 @@ __global__ __launch_bounds__(256) void absmax_cols_kernel(const void* __restrict
     for (int i = threadIdx.x; i < kColsPerWave; i += blockDim.x) {
         const int64_t col = static_cast<int64_t>(blockIdx.x) * kColsPerWave + i;
         if (col < C) {
-            float v = fmaxf(fmaxf(part[0][i], part[1][i]), fmaxf(part[2][i], part[3][i]));
-            atomic_max_nonneg(out + col, v);
+            float mv = fmaxf(fmaxf(part[0][i], part[1][i]), fmaxf(part[2][i], part[3][i]));
+            atomic_max_nonneg(out + col, mv);
         }
     }
 }
 
-// Row maxima: one wave per row, 16-byte chunks strided by the wave.
+// s_j = ax^alpha / aw^(1-alpha).  alpha = 0.5: correctly rounded roots and division; alpha = 1 and
+// alpha = 0 reduce to ax and 1/aw exactly; otherwise pow in double, rounded once to fp32.
+__device__ __forceinline__ float smooth_factor(float a, float b, float alpha) {
+    if (a == 0.0f || b == 0.0f) return 1.0f;
+    if (alpha == 0.5f) return div_rn(__builtin_sqrtf(a), __builtin_sqrtf(b));
+    if (alpha == 1.0f) return a;
+    if (alpha == 0.0f) return div_rn(1.0f, b);
+    return static_cast<float>(pow(static_cast<double>(a), static_cast<double>(alpha)) /
+                              pow(static_cast<double>(b), 1.0 - static_cast<double>(alpha)));
+}
+
+// Row maxima: one wave per row, 8 chunks of 16 bytes in flight per lane per iteration (chunks past
+// the row end re-read the last one).  With ax != NULL the row index is the channel j of the
+// smoothing factors and the wave also writes s[j] = smooth_factor(ax[j], max_n |W[j, n]|, alpha);
+// ax is complete when this kernel starts (the column maxima are computed by an earlier launch on
+// the same stream).
 template <bool kBf16, bool kVec>
 __global__ __launch_bounds__(256) void absmax_rows_kernel(const void* __restrict__ a, int64_t R, int64_t C,
-                                                          float* __restrict__ out) {
+                                                          float* __restrict__ out, const float* __restrict__ ax,
+                                                          float alpha, float* __restrict__ s) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + wave;
     if (r >= R) return;
+    const int64_t last = kVec ? C - 8 : C - 1;
     float m = 0.0f;
-    for (int64_t c = static_cast<int64_t>(lane) * 8; c < C; c += kColsPerWave) {
-        float v[8];
-        load_chunk<kBf16, kVec>(a, r * C, c, C, v);
+    for (int64_t c0 = static_cast<int64_t>(lane) * 8; c0 < C; c0 += 8 * kColsPerWave) {
+        float v[8][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+        for (int u = 0; u < 8; ++u) {
+            const int64_t c = c0 + u * kColsPerWave;
+            load_chunk<kBf16, kVec>(a, r * C, c < C ? c : last, C, v[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[u][e]));
     }
     m = wave_max(m);
-    if (lane == 0) out[r] = m;
+    if (lane == 0) {
+        out[r] = m;
+        if (ax) s[r] = smooth_factor(ax[r], m, alpha);
+    }
 }
 
-// s_j = ax^alpha / aw^(1-alpha).  alpha = 0.5: correctly rounded roots and division; alpha = 1 and
-// alpha = 0 reduce to ax and 1/aw exactly; otherwise pow in double, rounded once to fp32.
 __global__ void smooth_factors_kernel(const float* __restrict__ ax, const float* __restrict__ aw, int64_t K,
                                       float alpha, float* __restrict__ s) {
     int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (j >= K) return;
-    const float a = ax[j], b = aw[j];
-    float r;
-    if (a == 0.0f || b == 0.0f) r = 1.0f;
-    else if (alpha == 0.5f) r = div_rn(__builtin_sqrtf(a), __builtin_sqrtf(b));
-    else if (alpha == 1.0f) r = a;
-    else if (alpha == 0.0f) r = div_rn(1.0f, b);
-    else r = static_cast<float>(pow(static_cast<double>(a), static_cast<double>(alpha)) /
-                                pow(static_cast<double>(b), 1.0 - static_cast<double>(alpha)));
-    s[j] = r;
+    s[j] = smooth_factor(ax[j], aw[j], alpha);
+}
+
+template <bool kBf16, bool kVec>
+void cols_launch(dim3 grid, const void* a, int64_t R, int64_t C, const float* row_scale, float* out, hipStream_t st) {
+    if (row_scale)
+        hipLaunchKernelGGL((absmax_cols_kernel<kBf16, kVec, true>), grid, dim3(256), 0, st, a, R, C, row_scale, out);
+    else
+        hipLaunchKernelGGL((absmax_cols_kernel<kBf16, kVec, false>), grid, dim3(256), 0, st, a, R, C, row_scale, out);
 }
 
 }  // namespace
@@ -124,25 +157,26 @@ hipError_t launch_absmax_cols(const void* a, bool bf16, int64_t R, int64_t C, co
               static_cast<unsigned>((R + kRowsPerBlock - 1) / kRowsPerBlock));
     const bool vec = (C % 8) == 0;
     if (bf16) {
-        if (vec) hipLaunchKernelGGL((absmax_cols_kernel<true, true>), grid, dim3(256), 0, st, a, R, C, row_scale, out);
-        else hipLaunchKernelGGL((absmax_cols_kernel<true, false>), grid, dim3(256), 0, st, a, R, C, row_scale, out);
+        if (vec) cols_launch<true, true>(grid, a, R, C, row_scale, out, st);
+        else cols_launch<true, false>(grid, a, R, C, row_scale, out, st);
     } else {
-        if (vec) hipLaunchKernelGGL((absmax_cols_kernel<false, true>), grid, dim3(256), 0, st, a, R, C, row_scale, out);
-        else hipLaunchKernelGGL((absmax_cols_kernel<false, false>), grid, dim3(256), 0, st, a, R, C, row_scale, out);
+        if (vec) cols_launch<false, true>(grid, a, R, C, row_scale, out, st);
+        else cols_launch<false, false>(grid, a, R, C, row_scale, out, st);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_absmax_rows(const void* a, bool bf16, int64_t R, int64_t C, float* out, hipStream_t st) {
+hipError_t launch_absmax_rows(const void* a, bool bf16, int64_t R, int64_t C, float* out, const float* ax,
+                              float alpha, float* s, hipStream_t st) {
     if (R <= 0) return hipSuccess;
     dim3 grid(static_cast<unsigned>((R + 3) / 4));
     const bool vec = (C % 8) == 0;
     if (bf16) {
-        if (vec) hipLaunchKernelGGL((absmax_rows_kernel<true, true>), grid, dim3(256), 0, st, a, R, C, out);
-        else hipLaunchKernelGGL((absmax_rows_kernel<true, false>), grid, dim3(256), 0, st, a, R, C, out);
+        if (vec) hipLaunchKernelGGL((absmax_rows_kernel<true, true>), grid, dim3(256), 0, st, a, R, C, out, ax, alpha, s);
+        else hipLaunchKernelGGL((absmax_rows_kernel<true, false>), grid, dim3(256), 0, st, a, R, C, out, ax, alpha, s);
     } else {
-        if (vec) hipLaunchKernelGGL((absmax_rows_kernel<false, true>), grid, dim3(256), 0, st, a, R, C, out);
-        else hipLaunchKernelGGL((absmax_rows_kernel<false, false>), grid, dim3(256), 0, st, a, R, C, out);
+        if (vec) hipLaunchKernelGGL((absmax_rows_kernel<false, true>), grid, dim3(256), 0, st, a, R, C, out, ax, alpha, s);
+        else hipLaunchKernelGGL((absmax_rows_kernel<false, false>), grid, dim3(256), 0, st, a, R, C, out, ax, alpha, s);
     }
     return hipGetLastError();
 }

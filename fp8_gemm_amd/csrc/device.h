@@ -17,6 +17,39 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// 8 elements as loaded, before conversion: one 16-byte load for bf16, two for float32.  Loading
+// raw chunks first and converting later lets a wave keep many loads in flight with few registers.
+template <bool kBf16>
+struct Raw8 {
+    uint4 u[kBf16 ? 1 : 2];
+};
+
+template <bool kBf16>
+__device__ __forceinline__ Raw8<kBf16> load_raw8(const void* base, int64_t elem) {
+    Raw8<kBf16> r;
+    if constexpr (kBf16) {
+        r.u[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+    } else {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + elem);
+        r.u[0] = p[0];
+        r.u[1] = p[1];
+    }
+    return r;
+}
+
+template <bool kBf16>
+__device__ __forceinline__ void unpack8(const Raw8<kBf16>& r, float (&v)[8]) {
+    if constexpr (kBf16) {
+        const uint4 u = r.u[0];
+        v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+        v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z); v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+    } else {
+        const uint4 a = r.u[0], b = r.u[1];
+        v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+        v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+    }
+}
+
 template <bool kBf16>
 __device__ __forceinline__ void load8(const void* base, int64_t elem, float (&v)[8]) {
     if constexpr (kBf16) {
@@ -50,6 +83,32 @@ __device__ __forceinline__ void atomic_max_nonneg(float* addr, float v) {
 // IEEE fp32 division, correctly rounded (not a reciprocal multiply).
 __device__ __forceinline__ float div_rn(float a, float b) { return __fdiv_rn(a, b); }
 
+// a / b correctly rounded from rb = div_rn(1, b), in five operations instead of a full division
+// (Markstein, IBM J. Res. Dev. 34(1), 1990; Muller et al., "Handbook of Floating-Point
+// Arithmetic", the theorem on FMA-based division).  q0 = a * rb is within 1.5 ulp of a / b; the
+// first correction makes it faithful (within 1 ulp), and with a faithful quotient and the
+// correctly rounded reciprocal the second correction returns the correctly rounded a / b.  The
+// remainders are exact when nothing underflows: callers use this only where |b| and the quotients
+// that can affect a result lie well inside the normal range, and fall back to div_rn elsewhere.
+// The corrections turn a zero quotient into +0; kZeroSign restores the sign of a zero quotient
+// from q0 (needed where the sign of zero reaches a result, as in E4M3 codes).
+template <bool kZeroSign = true>
+__device__ __forceinline__ float div_by_rcp(float a, float b, float rb) {
+    const float q0 = a * rb;
+    const float r0 = __builtin_fmaf(-q0, b, a);
+    const float q1 = __builtin_fmaf(r0, rb, q0);
+    const float r1 = __builtin_fmaf(-q1, b, a);
+    const float q = __builtin_fmaf(r1, rb, q1);
+    return kZeroSign ? __builtin_copysignf(q, q0) : q;
+}
+
+// Divisors for which div_by_rcp is used: 2^lo <= |b| <= 2^hi.
+template <int kLo, int kHi>
+__device__ __forceinline__ bool in_pow2_range(float b) {
+    const float m = fabsf(b);
+    return m >= __builtin_ldexpf(1.0f, kLo) && m <= __builtin_ldexpf(1.0f, kHi);
+}
+
 // Symmetric INT8 code of v / scale: round half to even, clamp to [-127, 127].
 __device__ __forceinline__ int int8_code(float q) {
     float r = __builtin_rintf(q);
@@ -76,14 +135,37 @@ __device__ __forceinline__ uint32_t e4m3_code(float q) {
     return sign | mag;
 }
 
+// Code of a quotient q = v / scale (already divided).
+template <bool kFp8>
+__device__ __forceinline__ uint32_t code_of_q(float q) {
+    if constexpr (kFp8) {
+        return e4m3_code(fminf(fmaxf(q, -448.0f), 448.0f));
+    } else {
+        return static_cast<uint32_t>(int8_code(q)) & 0xFFu;
+    }
+}
+
 template <bool kFp8>
 __device__ __forceinline__ uint32_t code_of(float xs, float scale) {
+    return code_of_q<kFp8>(div_rn(xs, scale));
+}
+
+// Four codes of quotients packed into a word, q[0] in the low byte.
+// INT8: q is clamped to [-127, 127] (clamping before rounding gives the same integer as rounding
+// before clamping) and 1.5 * 2^23 is added: the sum's spacing is 1, so the addition rounds q to
+// an integer with ties to even, and the low byte of the sum's bit pattern is that integer in two's
+// complement.  Two byte permutes and an or gather the four low bytes.
+template <bool kFp8>
+__device__ __forceinline__ uint32_t pack_codes4(float q0, float q1, float q2, float q3) {
     if constexpr (kFp8) {
-        float q = div_rn(xs, scale);
-        q = fminf(fmaxf(q, -448.0f), 448.0f);
-        return e4m3_code(q);
+        return code_of_q<true>(q0) | (code_of_q<true>(q1) << 8) | (code_of_q<true>(q2) << 16) |
+               (code_of_q<true>(q3) << 24);
     } else {
-        return static_cast<uint32_t>(int8_code(div_rn(xs, scale))) & 0xFFu;
+        auto rounded = [](float q) { return __float_as_uint(fminf(fmaxf(q, -127.0f), 127.0f) + 12582912.0f); };
+        // v_perm_b32 selectors: 0-3 pick bytes of the second operand, 4-7 of the first, 0x0c gives 0.
+        const uint32_t lo = __builtin_amdgcn_perm(rounded(q1), rounded(q0), 0x0c0c0400u);
+        const uint32_t hi = __builtin_amdgcn_perm(rounded(q3), rounded(q2), 0x04000c0cu);
+        return lo | hi;
     }
 }
 

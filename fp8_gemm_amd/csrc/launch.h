@@ -16,7 +16,9 @@ hipError_t launch_absmax_cols(const void* a, bool bf16, int64_t R, int64_t C, co
                               float* out, hipStream_t st);
 
 // out[r] = max_c |a[r, c]| for a row-major [R, C] matrix (one wave per row, no atomics).
-hipError_t launch_absmax_rows(const void* a, bool bf16, int64_t R, int64_t C, float* out, hipStream_t st);
+// Row maxima of a [R, C]; with ax != NULL also s[r] = smoothing factor of (ax[r], out[r]).
+hipError_t launch_absmax_rows(const void* a, bool bf16, int64_t R, int64_t C, float* out, const float* ax,
+                              float alpha, float* s, hipStream_t st);
 
 // s[j] = ax[j]^alpha / aw[j]^(1-alpha), s = 1 where a maximum is 0.
 hipError_t launch_smooth_factors(const float* ax, const float* aw, int64_t K, float alpha, float* s,

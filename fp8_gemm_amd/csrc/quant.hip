@@ -2,6 +2,8 @@
 // ("Weight-Activation Quantization", section 3: divide activation channel j by s_j, multiply
 // weight channel j by s_j, then X_int8 = quantize(X_tilde), W_int8 = quantize(W_tilde); section 2:
 // symmetric INT8 with scale = absmax / 127; section 4: E4M3 with scale = absmax / 448.)
+#include <algorithm>
+
 #include "device.h"
 #include "launch.h"
 
@@ -11,57 +13,164 @@ namespace {
 
 // ---- activations: one wave per row ---------------------------------------------------------------
 //
-// The row is read once from HBM into registers (kChunks 16-byte chunks of 8 elements per lane),
-// divided by s, reduced to its maximum with a wave butterfly, and quantized from registers.
-// Lane l owns chunks l, l + 64, l + 128, ... so every load instruction of the wave reads 512
-// consecutive elements.
-template <bool kBf16, bool kFp8, int kChunks>
-__global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__ x, const float* __restrict__ s,
-                                                        int64_t M, int64_t K, uint8_t* __restrict__ q,
-                                                        float* __restrict__ scale) {
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-    if (row >= M) return;
-    const int64_t nchunk = K / 8;
-    float v[kChunks][8];
+// A block of kActWaves waves quantizes whole rows, each wave `rows_per_wave` of them in turn.  The
+// block first stages s and its correctly rounded reciprocals in LDS, so that every X / s and every
+// X~ / scale is a five-operation correctly rounded division (div_by_rcp) instead of a full one.
+// A row is read once from HBM into registers (kChunks 16-byte chunks of 8 elements per lane), lane
+// l owning chunks l, l + 64, ..., so that each load instruction of the wave reads 512 consecutive
+// elements; it is divided by s, reduced to its maximum with a wave butterfly, and quantized from
+// registers.
+//
+// Fast-division guards (outside them the full division is used, with identical results):
+//   - every s[j] of the block in [2^-20, 2^20];
+//   - the row scale in [2^-60, 2^60].
+// Then every element whose code can be nonzero, and the row maximum, has X~ >= 2^-10 * scale >=
+// 2^-70 and X >= 2^-90, so all quotients and remainders are normal numbers and exact; elements
+// below that bound give code 0 on either path.
+constexpr int kActWaves = 8;
+
+// LDS layout of s and 1/s: for chunk c (elements 8c .. 8c + 7), the low halves 8c .. 8c + 3 of all
+// chunks come first, then the high halves, so that the 16-byte reads of consecutive lanes are
+// consecutive (free of bank conflicts).
+__device__ __forceinline__ int lds_half(int64_t j, int64_t nchunk) {
+    const int64_t c = j >> 3, e = j & 7;
+    return static_cast<int>((e >> 2) * nchunk * 4 + c * 4 + (e & 3));
+}
+
+template <bool kFast, bool kSmooth, bool kFp8, int kChunks>
+__device__ __forceinline__ float smooth_chunks(float (&v)[kChunks][8], const float* sh_s, const float* sh_r,
+                                               int lane_c, int stride, int64_t nchunk) {
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
-        const int64_t c = lane + static_cast<int64_t>(kWave) * i;
-        if (c < nchunk) {
-            load8<kBf16>(x, row * K + c * 8, v[i]);
-            if (s) {
-                float sv[8];
-                load8<false>(s, c * 8, sv);
+        int64_t c = lane_c + static_cast<int64_t>(stride) * i;
+        c = c < nchunk ? c : nchunk - 1;
+        {
+            if constexpr (kSmooth) {
+                const float4 s0 = *reinterpret_cast<const float4*>(sh_s + c * 4);
+                const float4 s1 = *reinterpret_cast<const float4*>(sh_s + (nchunk + c) * 4);
+                const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+                if constexpr (kFast) {
+                    const float4 r0 = *reinterpret_cast<const float4*>(sh_r + c * 4);
+                    const float4 r1 = *reinterpret_cast<const float4*>(sh_r + (nchunk + c) * 4);
+                    const float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[i][e] = div_rn(v[i][e], sv[e]);
+                    for (int e = 0; e < 8; ++e) v[i][e] = div_by_rcp<kFp8>(v[i][e], sv[e], rv[e]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[i][e] = div_rn(v[i][e], sv[e]);
+                }
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
         }
     }
-    amax = wave_max(amax);
-    const float sc = div_rn(amax, qmax<kFp8>());
-    if (lane == 0) scale[row] = sc;
+    return amax;
+}
+
+template <bool kFp8, bool kFast, int kChunks>
+__device__ __forceinline__ void store_codes(const float (&v)[kChunks][8], float sc, float rsc, int lane_c,
+                                            int stride, int64_t nchunk, uint8_t* __restrict__ qrow) {
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
-        const int64_t c = lane + static_cast<int64_t>(kWave) * i;
+        const int64_t c = lane_c + static_cast<int64_t>(stride) * i;
         if (c < nchunk) {
-            uint32_t lo = 0, hi = 0;
-            if (amax != 0.0f) {
+            float qv[8];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    lo |= code_of<kFp8>(v[i][e], sc) << (8 * e);
-                    hi |= code_of<kFp8>(v[i][e + 4], sc) << (8 * e);
-                }
-            }
-            *reinterpret_cast<uint2*>(q + row * K + c * 8) = make_uint2(lo, hi);
+            for (int e = 0; e < 8; ++e) qv[e] = kFast ? div_by_rcp<kFp8>(v[i][e], sc, rsc) : div_rn(v[i][e], sc);
+            const uint32_t lo = pack_codes4<kFp8>(qv[0], qv[1], qv[2], qv[3]);
+            const uint32_t hi = pack_codes4<kFp8>(qv[4], qv[5], qv[6], qv[7]);
+            *reinterpret_cast<uint2*>(qrow + c * 8) = make_uint2(lo, hi);
         }
     }
 }
 
-// Rows longer than the register-resident variants: two passes over the row (the second mostly
-// hits the cache), same arithmetic.
+template <bool kBf16, bool kFp8, int kChunks, bool kSmooth, bool kPair>
+__global__ __launch_bounds__(kActWaves * kWave) void quant_act_kernel(
+    const void* __restrict__ x, const float* __restrict__ s, int64_t M, int64_t K, int rows_per_wave,
+    uint8_t* __restrict__ q, float* __restrict__ scale) {
+    extern __shared__ float sh[];               // kSmooth: s then 1/s, each K floats (lds_half order)
+    __shared__ float xchg[2][kActWaves];        // kPair: the two halves' maxima of a row
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int64_t nchunk = K / 8;
+    float* const sh_s = sh;
+    float* const sh_r = sh + K;
+    bool fast_s = true;
+    if constexpr (kSmooth) {
+        // K <= (kPair ? 2 : 1) * kChunks * 512: at most that many elements per thread, loaded
+        // together (indices past K re-read s[K - 1] and are not stored).
+        constexpr int kPer = (kPair ? 2 : 1) * kChunks;
+        float sv[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int64_t j = threadIdx.x + static_cast<int64_t>(i) * blockDim.x;
+            sv[i] = s[j < K ? j : K - 1];
+        }
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int64_t j = threadIdx.x + static_cast<int64_t>(i) * blockDim.x;
+            if (j < K) {
+                const int h = lds_half(j, nchunk);
+                sh_s[h] = sv[i];
+                sh_r[h] = div_rn(1.0f, sv[i]);
+                fast_s = fast_s && in_pow2_range<-20, 20>(sv[i]);
+            }
+        }
+        fast_s = __syncthreads_and(fast_s);
+    }
+    // A row is handled by one wave, or (kPair) by the waves 2p and 2p + 1, which take alternate
+    // 512-element blocks of it.
+    constexpr int kRowsPerPass = kPair ? kActWaves / 2 : kActWaves;
+    const int slot = kPair ? wave / 2 : wave;
+    const int part = kPair ? wave % 2 : 0;
+    const int lane_c = part * kWave + lane;     // first chunk of this wave's share
+    constexpr int kStride = (kPair ? 2 : 1) * kWave;
+    for (int rr = 0; rr < rows_per_wave; ++rr) {
+        const int64_t row = (static_cast<int64_t>(blockIdx.x) * rows_per_wave + rr) * kRowsPerPass + slot;
+        const bool live = row < M;
+        if (!kPair && !live) break;
+        const int64_t rrow = live ? row : M - 1;
+        // All loads unconditional (chunks past the row end re-read the last chunk, which changes
+        // no maximum and is never stored) and issued before any conversion, so that they are all
+        // in flight at once.
+        Raw8<kBf16> raw[kChunks];
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) {
+            int64_t c = lane_c + static_cast<int64_t>(kStride) * i;
+            c = c < nchunk ? c : nchunk - 1;
+            raw[i] = load_raw8<kBf16>(x, rrow * K + c * 8);
+        }
+        float v[kChunks][8];
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) unpack8<kBf16>(raw[i], v[i]);
+        float amax = fast_s ? smooth_chunks<true, kSmooth, kFp8>(v, sh_s, sh_r, lane_c, kStride, nchunk)
+                            : smooth_chunks<false, kSmooth, kFp8>(v, sh_s, sh_r, lane_c, kStride, nchunk);
+        amax = wave_max(amax);
+        if constexpr (kPair) {
+            if (lane == 0) xchg[rr & 1][wave] = amax;
+            __syncthreads();
+            amax = fmaxf(amax, xchg[rr & 1][wave ^ 1]);
+        }
+        if (!live) continue;
+        const float sc = div_rn(amax, qmax<kFp8>());
+        if (lane == 0 && part == 0) scale[row] = sc;
+        uint8_t* const qrow = q + row * K;
+        if (amax == 0.0f) {
+#pragma unroll
+            for (int i = 0; i < kChunks; ++i) {
+                const int64_t c = lane_c + static_cast<int64_t>(kStride) * i;
+                if (c < nchunk) *reinterpret_cast<uint2*>(qrow + c * 8) = make_uint2(0u, 0u);
+            }
+        } else if (in_pow2_range<-60, 60>(sc)) {
+            store_codes<kFp8, true>(v, sc, div_rn(1.0f, sc), lane_c, kStride, nchunk, qrow);
+        } else {
+            store_codes<kFp8, false>(v, sc, 0.0f, lane_c, kStride, nchunk, qrow);
+        }
+    }
+}
+
+// Rows longer than the register-resident variants (K > 8192): two passes over the row (the second
+// mostly hits the cache), full divisions.
 template <bool kBf16, bool kFp8>
 __global__ __launch_bounds__(256) void quant_act_long_kernel(const void* __restrict__ x, const float* __restrict__ s,
                                                              int64_t M, int64_t K, uint8_t* __restrict__ q,
@@ -109,11 +218,25 @@ __global__ __launch_bounds__(256) void quant_act_long_kernel(const void* __restr
 
 // ---- weights: W~ = s * W [K, N] -> codes transposed to wq [N, K] --------------------------------
 //
-// A block owns a tile of kTJ rows (j) x kTN columns (n) of W.  It reads the tile row by row
-// (coalesced along n), forms W~ = s[j] * W[j, n] and its code with the column's scale, writes the
-// codes into LDS as [n][j], and stores them as rows of wq (contiguous along j).
-constexpr int kTJ = 128;
-constexpr int kTN = 64;
+// A block of 256 threads owns a tile of kTJ = 256 rows (j) x kTN = 128 columns (n) of W.  Loads are
+// coalesced along n: a wave instruction reads 8 rows x 128 bytes.  Each thread handles 8 columns x
+// 4 consecutive rows at a time, forms W~ = s[j] * W[j, n] and the codes with the column scales, and
+// packs the 4 codes of one column (rows j .. j + 3) into one LDS word; the tile is stored transposed,
+// one row of kTJ / 4 words per column n, and written back as 16-byte pieces of wq rows (contiguous
+// along j).
+//
+// LDS word of (column c, row group g = j / 4): c * kTStride + (g ^ (8 * ((c / 8) % 8))).  The row
+// stride kTStride = 72 = 8 (mod 64) and the xor make the 64 words one wave writes at a time (8 row
+// groups x 8 column chunks) fall in 64 different banks; a 16-byte read of 4 consecutive words
+// returns 4 consecutive row groups (the xor only moves whole aligned groups of 8).
+//
+// Codes use div_by_rcp with each column's correctly rounded 1 / scale when every column scale of
+// the block lies in [2^-60, 2^60] (or its maximum is 0: codes 0); then every W~ whose code can be
+// nonzero is at least 2^-70 and its quotient and remainders are normal.  Otherwise the block
+// divides in full.
+constexpr int kTJ = 256;
+constexpr int kTN = 128;
+constexpr int kTStride = kTJ / 4 + 8;
 
 template <bool kBf16>
 __device__ __forceinline__ float load1(const void* base, int64_t i) {
@@ -121,65 +244,110 @@ __device__ __forceinline__ float load1(const void* base, int64_t i) {
     else return static_cast<const float*>(base)[i];
 }
 
+// Loads of one (row group, column chunk) item: rows j .. j + 3, columns n .. n + 7.  Unconditional
+// (rows past K and columns past N re-read the last ones; their codes land in tile positions that
+// are never stored), so that all of a thread's loads are in flight at once.
+template <bool kBf16, bool kVec>
+struct WeightItem {
+    Raw8<kBf16> raw[4];       // kVec
+    float val[kVec ? 1 : 4][kVec ? 1 : 8];
+};
+
+template <bool kBf16, bool kVec>
+__device__ __forceinline__ void load_item(const void* __restrict__ w, int64_t K, int64_t N, int64_t j, int64_t n,
+                                          WeightItem<kBf16, kVec>& it) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t jr = (j + i < K) ? j + i : K - 1;
+        if constexpr (kVec) {
+            it.raw[i] = load_raw8<kBf16>(w, jr * N + (n < N ? n : N - 8));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) it.val[i][e] = load1<kBf16>(w, jr * N + (n + e < N ? n + e : N - 1));
+        }
+    }
+}
+
+template <bool kBf16, bool kFp8, bool kVec, bool kFast>
+__device__ __forceinline__ void code_item(const WeightItem<kBf16, kVec>& it, const float (&sj)[4],
+                                          const float* col_amax, const float* col_scale, const float* col_rcp,
+                                          int cl0, uint32_t* __restrict__ tile, int g) {
+    float v[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (kVec) {
+            unpack8<kBf16>(it.raw[i], v[i]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[i][e] = it.val[i][e];
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int c = cl0 + e;
+        const float sc = col_scale[c];
+        float qv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float ws = sj[i] * v[i][e];
+            qv[i] = kFast ? div_by_rcp<kFp8>(ws, sc, col_rcp[c]) : div_rn(ws, sc);
+        }
+        const uint32_t word = (col_amax[c] != 0.0f) ? pack_codes4<kFp8>(qv[0], qv[1], qv[2], qv[3]) : 0u;
+        tile[c * kTStride + (g ^ (8 * ((c >> 3) & 7)))] = word;
+    }
+}
+
 template <bool kBf16, bool kFp8, bool kVec>
 __global__ __launch_bounds__(256) void quant_weight_t_kernel(const void* __restrict__ w, int64_t K, int64_t N,
                                                              const float* __restrict__ s,
                                                              const float* __restrict__ amax,
                                                              uint8_t* __restrict__ wq) {
-    __shared__ uint8_t tile[kTN][kTJ + 4];
-    __shared__ float col_scale[kTN];
-    __shared__ float col_amax[kTN];
+    __shared__ uint32_t tile[kTN * kTStride];
+    __shared__ float col_amax[kTN], col_scale[kTN], col_rcp[kTN], row_s[kTJ];
     const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kTN;
     const int64_t j0 = static_cast<int64_t>(blockIdx.y) * kTJ;
+    bool fast = true;
     if (threadIdx.x < kTN) {
         const int64_t n = n0 + threadIdx.x;
         const float a = (n < N) ? amax[n] : 0.0f;
+        const float sc = div_rn(a, qmax<kFp8>());
         col_amax[threadIdx.x] = a;
-        col_scale[threadIdx.x] = div_rn(a, qmax<kFp8>());
+        col_scale[threadIdx.x] = sc;
+        col_rcp[threadIdx.x] = div_rn(1.0f, sc);
+        fast = a == 0.0f || in_pow2_range<-60, 60>(sc);
+    }
+    {
+        const int64_t j = j0 + threadIdx.x;
+        row_s[threadIdx.x] = (s && j < K) ? s[j] : 1.0f;
+    }
+    fast = __syncthreads_and(fast);
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int cl = lane & 7, rl = lane >> 3;
+    // 64 row groups x 16 column chunks, 4 (group, chunk) items per thread.  Item it of wave w is
+    // combination b = 4 w + it: column chunk cc = cl + 8 (b / 8), row group g = rl + 8 (b % 8).
+    WeightItem<kBf16, kVec> items[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int b = wave * 4 + it;
+        const int cc = cl + 8 * (b >> 3), g = rl + 8 * (b & 7);
+        load_item<kBf16, kVec>(w, K, N, j0 + 4 * g, n0 + 8 * cc, items[it]);
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int b = wave * 4 + it;
+        const int cc = cl + 8 * (b >> 3), g = rl + 8 * (b & 7);
+        const float sj[4] = {row_s[4 * g], row_s[4 * g + 1], row_s[4 * g + 2], row_s[4 * g + 3]};
+        if (fast) code_item<kBf16, kFp8, kVec, true>(items[it], sj, col_amax, col_scale, col_rcp, 8 * cc, tile, g);
+        else code_item<kBf16, kFp8, kVec, false>(items[it], sj, col_amax, col_scale, col_rcp, 8 * cc, tile, g);
     }
     __syncthreads();
-    // kTJ rows x (kTN / 8) chunks of 8 columns = 1024 chunks, 4 per thread.
-    for (int idx = threadIdx.x; idx < kTJ * (kTN / 8); idx += blockDim.x) {
-        const int jl = idx / (kTN / 8);
-        const int cl = (idx % (kTN / 8)) * 8;
-        const int64_t j = j0 + jl;
-        const int64_t n = n0 + cl;
-        float v[8];
-        if (j < K && n < N) {
-            if constexpr (kVec) {
-                load8<kBf16>(w, j * N + n, v);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = (n + e < N) ? load1<kBf16>(w, j * N + n + e) : 0.0f;
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = 0.0f;
-        }
-        const float sj = (s && j < K) ? s[j] : 1.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float ws = s ? sj * v[e] : v[e];
-            const uint32_t code = (col_amax[cl + e] != 0.0f) ? code_of<kFp8>(ws, col_scale[cl + e]) : 0u;
-            tile[cl + e][jl] = static_cast<uint8_t>(code);
-        }
-    }
-    __syncthreads();
-    // kTN rows of kTJ bytes = 64 x 8 chunks of 16 bytes, 2 per thread.
+    // Row n0 + c of wq gets 16-byte piece t (tile rows 16 t .. 16 t + 15 = row groups 4 t .. 4 t + 3,
+    // stored at word 4 (t ^ 2 ((c / 8) % 8))).  16 consecutive threads read one column's 256 bytes.
     for (int idx = threadIdx.x; idx < kTN * (kTJ / 16); idx += blockDim.x) {
-        const int nl = idx / (kTJ / 16);
-        const int jc = (idx % (kTJ / 16)) * 16;
-        const int64_t n = n0 + nl;
-        const int64_t j = j0 + jc;
-        if (n < N && j < K) {   // K is a multiple of 16: a 16-byte chunk is all in or all out
-            const uint8_t* src = &tile[nl][jc];
-            uint4 u;
-            u.x = src[0] | (src[1] << 8) | (src[2] << 16) | (static_cast<uint32_t>(src[3]) << 24);
-            u.y = src[4] | (src[5] << 8) | (src[6] << 16) | (static_cast<uint32_t>(src[7]) << 24);
-            u.z = src[8] | (src[9] << 8) | (src[10] << 16) | (static_cast<uint32_t>(src[11]) << 24);
-            u.w = src[12] | (src[13] << 8) | (src[14] << 16) | (static_cast<uint32_t>(src[15]) << 24);
-            *reinterpret_cast<uint4*>(wq + n * K + j) = u;
-        }
+        const int c = idx / (kTJ / 16), t = idx % (kTJ / 16);
+        const int64_t n = n0 + c, j = j0 + 16 * t;
+        const uint4 u = *reinterpret_cast<const uint4*>(&tile[c * kTStride + 4 * (t ^ (2 * ((c >> 3) & 7)))]);
+        if (n < N && j < K) *reinterpret_cast<uint4*>(wq + n * K + j) = u;   // K % 16 == 0
     }
 }
 
@@ -188,17 +356,35 @@ __global__ void finalize_scales_kernel(float* p, int64_t n, float qm) {
     if (i < n) p[i] = div_rn(p[i], qm);
 }
 
+template <bool kBf16, bool kFp8, int kChunks, bool kPair>
+void quant_act_launch(const void* x, int64_t M, int64_t K, const float* s, uint8_t* xq, float* xs, hipStream_t st) {
+    // Rows per wave: one, or more once there are enough rows for two blocks per CU on 256 CUs.
+    const int64_t rows_per_pass = kPair ? kActWaves / 2 : kActWaves;
+    const int64_t rows_per_block_pass = rows_per_pass * 512;
+    const int rpw = static_cast<int>(std::max<int64_t>(1, (M + rows_per_block_pass - 1) / rows_per_block_pass));
+    const int64_t rows_per_block = rows_per_pass * rpw;
+    dim3 grid(static_cast<unsigned>((M + rows_per_block - 1) / rows_per_block)), block(kActWaves * kWave);
+    if (s) {
+        const size_t lds = 2 * static_cast<size_t>(K) * sizeof(float);
+        hipLaunchKernelGGL((quant_act_kernel<kBf16, kFp8, kChunks, true, kPair>), grid, block, lds, st, x, s, M, K, rpw,
+                           xq, xs);
+    } else {
+        hipLaunchKernelGGL((quant_act_kernel<kBf16, kFp8, kChunks, false, kPair>), grid, block, 0, st, x, s, M, K, rpw,
+                           xq, xs);
+    }
+}
+
 template <bool kBf16, bool kFp8>
 hipError_t quant_act_dispatch(const void* x, int64_t M, int64_t K, const float* s, uint8_t* xq, float* xs,
                               hipStream_t st) {
-    dim3 grid(static_cast<unsigned>((M + 3) / 4)), block(256);
     const int64_t per_lane = (K / 8 + kWave - 1) / kWave;
-    if (per_lane <= 1) hipLaunchKernelGGL((quant_act_kernel<kBf16, kFp8, 1>), grid, block, 0, st, x, s, M, K, xq, xs);
-    else if (per_lane <= 2) hipLaunchKernelGGL((quant_act_kernel<kBf16, kFp8, 2>), grid, block, 0, st, x, s, M, K, xq, xs);
-    else if (per_lane <= 4) hipLaunchKernelGGL((quant_act_kernel<kBf16, kFp8, 4>), grid, block, 0, st, x, s, M, K, xq, xs);
-    else if (per_lane <= 8) hipLaunchKernelGGL((quant_act_kernel<kBf16, kFp8, 8>), grid, block, 0, st, x, s, M, K, xq, xs);
-    else if (per_lane <= 16) hipLaunchKernelGGL((quant_act_kernel<kBf16, kFp8, 16>), grid, block, 0, st, x, s, M, K, xq, xs);
-    else hipLaunchKernelGGL((quant_act_long_kernel<kBf16, kFp8>), grid, block, 0, st, x, s, M, K, xq, xs);
+    if (per_lane <= 1) quant_act_launch<kBf16, kFp8, 1, false>(x, M, K, s, xq, xs, st);
+    else if (per_lane <= 2) quant_act_launch<kBf16, kFp8, 2, false>(x, M, K, s, xq, xs, st);
+    else if (per_lane <= 4) quant_act_launch<kBf16, kFp8, 4, false>(x, M, K, s, xq, xs, st);
+    else if (per_lane <= 8) quant_act_launch<kBf16, kFp8, 8, false>(x, M, K, s, xq, xs, st);
+    else if (per_lane <= 16) quant_act_launch<kBf16, kFp8, 8, true>(x, M, K, s, xq, xs, st);
+    else hipLaunchKernelGGL((quant_act_long_kernel<kBf16, kFp8>), dim3(static_cast<unsigned>((M + 3) / 4)), dim3(256), 0,
+                            st, x, s, M, K, xq, xs);
     return hipGetLastError();
 }
 

@@ -144,6 +144,51 @@ def test_accumulate_calibration(f):
     np.testing.assert_array_equal(host(s2), ref_s)
 
 
+def wide_matrix(shape, seed, lo, hi):
+    """float32 values with random signs, mantissas and binary exponents in [lo, hi]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    m = rng.uniform(1.0, 2.0, shape)
+    e = rng.integers(lo, hi + 1, shape)
+    sign = np.where(rng.random(shape) < 0.5, -1.0, 1.0)
+    return (sign * np.ldexp(m, e)).astype(np.float32)
+
+
+@pytest.mark.parametrize("qtype", ["int8", "fp8"])
+def test_division_paths_wide_range(f, qtype):
+    """Quantization divides by s and by the scales through a correctly rounded reciprocal and two
+    FMA corrections where divisor and quotients are in range, and with full divisions elsewhere.
+    Codes and scales must equal the oracle's true IEEE divisions bit for bit on both paths:
+    rows spanning 2^-40..2^40 with per-row peaks from 2^-75 (scale below the fast range) to 2^70,
+    subnormal entries, and smoothing factors inside [2^-18, 2^18] (fast) or partly outside (full)."""
+    M, K, N = 640, 1024, 384
+    announce(f"division paths {qtype} M={M} K={K} N={N}")
+    peak_e = np.random.Generator(np.random.PCG64(72)).integers(-75, 71, M)
+    X = wide_matrix((M, K), 71, -40, -1)                  # row m spans 2^(peak - 40) .. 2^peak
+    X = (X * np.ldexp(1.0, peak_e)[:, None]).astype(np.float32)
+    X[np.arange(M), (np.arange(M) * 7) % K] = np.ldexp(1.5, peak_e).astype(np.float32)
+    X[5, 3:9] = np.float32(1e-42)                      # subnormal inputs
+    X[6] = np.ldexp(np.float32(1.25), -130)            # a whole row of subnormals
+    W = wide_matrix((K, N), 73, -30, 30)
+    W[2, :4] = np.float32(3e-44)
+    X[9, 10:14] = np.float32(-0.0)                     # E4M3 keeps the sign of zero
+    W[7, :5] = np.float32(-0.0)
+    s_in = np.ldexp(np.random.Generator(np.random.PCG64(74)).uniform(1.0, 2.0, K), np.random.Generator(
+        np.random.PCG64(75)).integers(-18, 19, K)).astype(np.float32)
+    s_out = s_in.copy()
+    s_out[[3, 500]] = np.float32([2.0 ** -23, 2.0 ** 24])  # outside the fast range: full divisions
+    x, w = dev(X), dev(W)
+    for s in (s_in, s_out):
+        xq, sx = f.w8a8_quant_act(x, dev(s), qtype)
+        wq, sw = f.w8a8_fold_quant_weight(w, dev(s), qtype)
+        torch.cuda.synchronize()
+        qx_ref, sx_ref = oracle.quant_act(X, s, qtype)
+        qw_ref, sw_ref = oracle.fold_quant_weight(W, s, qtype)
+        np.testing.assert_array_equal(host(sx), sx_ref)
+        np.testing.assert_array_equal(host(xq).view(np.uint8), qx_ref.view(np.uint8))
+        np.testing.assert_array_equal(host(sw), sw_ref)
+        np.testing.assert_array_equal(host(wq).view(np.uint8), qw_ref.view(np.uint8))
+
+
 @pytest.mark.parametrize("alpha", [0.0, 1.0, 0.75])
 def test_alpha(f, alpha):
     announce(f"alpha={alpha}")
