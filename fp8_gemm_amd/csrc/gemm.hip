@@ -201,20 +201,21 @@ __device__ __forceinline__ void copy_v(uintptr_t src, uint32_t lds) {
 // loop.  Rows
 // past the end re-read the last row (never stored); in the last K step of a ragged K, chunks past
 // K come from g_zero16.
-template <int kRows>
+template <int kRows, int kWaves>
 struct CopyPlan {
-    static constexpr int kPerWave = kRows / 32;
+    static constexpr int kPerWave = kRows / (8 * kWaves);
+    static_assert(kPerWave * 8 * kWaves == kRows && kWaves % 2 == 0, "whole 1 KB blocks per wave");
     uint32_t off[kPerWave];
     int chunk;
 
     __device__ __forceinline__ void init(int64_t row0, int64_t rows, int64_t K, int wave, int lane) {
         const int rl = lane >> 3;
-        // copy i of this wave fills rows 8 * blk + rl, blk = wave + 4 i (so blk is odd iff wave is);
-        // its stored chunk lane % 8 holds logical chunk (lane % 8) ^ ((row >> 1) & 7).
+        // copy i of this wave fills rows 8 * blk + rl, blk = wave + kWaves * i (so blk is odd iff
+        // wave is); its stored chunk lane % 8 holds logical chunk (lane % 8) ^ ((row >> 1) & 7).
         chunk = (lane & 7) ^ ((4 * (wave & 1) + (rl >> 1)) & 7);
 #pragma unroll
         for (int i = 0; i < kPerWave; ++i) {
-            int64_t gr = row0 + (wave + 4 * i) * 8 + rl;
+            int64_t gr = row0 + (wave + kWaves * i) * 8 + rl;
             gr = gr < rows ? gr : rows - 1;
             off[i] = static_cast<uint32_t>((gr - row0) * K + chunk * 16);
         }
@@ -223,7 +224,7 @@ struct CopyPlan {
     // the K step's first byte (only looked at when !full_k).
     __device__ __forceinline__ void one(int i, const uint8_t* tile, const uint8_t* lds, int wave, bool full_k,
                                         int64_t k_left) const {
-        const uint32_t l = lds_addr(lds) + wave * 1024 + 4096 * i;
+        const uint32_t l = lds_addr(lds) + wave * 1024 + kWaves * 1024 * i;
         if (full_k) {
             copy_sv(tile, off[i], l);
         } else {
@@ -256,28 +257,34 @@ __device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_m,
     tn = in / gm;
 }
 
-template <int kBM, int kBN, typename MM, bool kOutAcc>
-__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_tile_kernel(
+template <int kBM, int kBN, int kGM, int kGN, int kStages, typename MM, bool kOutAcc>
+__global__ __launch_bounds__(kGM * kGN * kWave, 1)
+__attribute__((amdgpu_waves_per_eu(kGM * kGN / 4, kGM * kGN / 4))) void gemm_tile_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ x_scale, const uint8_t* __restrict__ wq,
     const float* __restrict__ w_scale, int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y,
     void* __restrict__ out_acc, int tiles_m, int tiles_n, int group_m) {
     using Acc = typename MM::Acc;
-    constexpr int kWM = kBM / 2, kWN = kBN / 2;
+    constexpr int kWaves = kGM * kGN;                 // a kGM x kGN grid of waves
+    constexpr int kWM = kBM / kGM, kWN = kBN / kGN;   // each wave's kWM x kWN outputs
     constexpr int kMT = kWM / MM::kTile, kNT = kWN / MM::kTile;
     constexpr int kC = MM::kChunks;
     constexpr int kSub = 64 / MM::kKStep;            // instructions per 64-byte half-step
     static_assert(kSub >= 1 && kSub * MM::kKStep == 64, "a half-step is 64 K bytes");
-    constexpr int kCopies = kBM / 32 + kBN / 32;     // copy instructions per wave per stage
-    // Three X stages, then three W stages; after the K loop the same LDS stages the bf16 output.
+    using CopyX = CopyPlan<kBM, kWaves>;
+    using CopyW = CopyPlan<kBN, kWaves>;
+    constexpr int kCopies = CopyX::kPerWave + CopyW::kPerWave;   // copy instructions per wave per stage
+    // kStages X stages, then kStages W stages; after the K loop the same LDS stages the bf16 output.
+    static_assert(kStages == 2 || kStages == 3, "two or three stages");
     constexpr int kOutStride = kWN * 2 + 16;         // bytes per staged output row (padded)
-    static_assert(4 * kWM * kOutStride <= 3 * (kBM + kBN) * kBK, "output staging fits in the stages");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[3 * (kBM + kBN) * kBK];
+    constexpr int kStageBytes = kStages * (kBM + kBN) * kBK;
+    constexpr int kOutBytes = kWaves * kWM * kOutStride;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kStageBytes > kOutBytes ? kStageBytes : kOutBytes];
     uint8_t* const xs0 = smem;
     uint8_t* const xs1 = smem + kBM * kBK;
-    uint8_t* const xs2 = smem + 2 * kBM * kBK;
-    uint8_t* const ws0 = smem + 3 * kBM * kBK;
+    uint8_t* const xs2 = smem + 2 * kBM * kBK;      // kStages == 3 only
+    uint8_t* const ws0 = smem + kStages * kBM * kBK;
     uint8_t* const ws1 = ws0 + kBN * kBK;
-    uint8_t* const ws2 = ws0 + 2 * kBN * kBK;
+    uint8_t* const ws2 = ws0 + 2 * kBN * kBK;       // kStages == 3 only
 
     int tm, tn;
     tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
@@ -286,7 +293,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     // LDS addresses of the copies, which must be scalar) in scalar registers.
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int lane = threadIdx.x % kWave;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / kGN, wn = wave % kGN;
     const int frag_row = lane % MM::kTile, frag_grp = lane / MM::kTile;
 
     Acc acc[kMT][kNT];
@@ -295,12 +302,14 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
         for (int j = 0; j < kNT; ++j) acc[i][j] = MM::zero();
 
-    // Scales of this lane's outputs, requested before the K loop so they arrive during it.
+    // Scales of this lane's outputs: requested before the K loop, so that they arrive during it,
+    // when the registers allow (small per-wave tiles); otherwise at the start of the epilogue.
     constexpr int kG = MM::kGroups;
+    constexpr bool kPreloadScales = kMT * kNT <= 8;
     const int64_t mw0 = m0 + wm * kWM, nw0 = n0 + wn * kWN;
     float sx_l[kMT];
     v4f sw_l[kNT][kG];
-    if constexpr (!kOutAcc) {
+    auto load_scales = [&]() {
 #pragma unroll
         for (int i = 0; i < kMT; ++i) {
             const int64_t m = mw0 + i * MM::kTile + out_row<MM::kTile>(lane);
@@ -318,25 +327,30 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
                     for (int r = 0; r < 4; ++r) sw_l[j][g][r] = (n + r < N) ? w_scale[n + r] : 0.0f;
                 }
             }
-    }
+    };
+    if constexpr (!kOutAcc && kPreloadScales) load_scales();
 
     const int nk = static_cast<int>((K + kBK - 1) / kBK);
     const bool ragged_k = (K % kBK) != 0;
-    CopyPlan<kBM> cx;
-    CopyPlan<kBN> cw;
+    CopyX cx;
+    CopyW cw;
     cx.init(m0, M, K, wave, lane);
     cw.init(n0, N, K, wave, lane);
     const uint8_t* xtile = xq + m0 * K;
     const uint8_t* wtile = wq + n0 * K;
-    auto stage_x = [&](int kt) { return kt % 3 == 0 ? xs0 : (kt % 3 == 1 ? xs1 : xs2); };
-    auto stage_w = [&](int kt) { return kt % 3 == 0 ? ws0 : (kt % 3 == 1 ? ws1 : ws2); };
+    auto stage_x = [&](int kt) {
+        return kStages == 2 ? ((kt & 1) ? xs1 : xs0) : (kt % 3 == 0 ? xs0 : (kt % 3 == 1 ? xs1 : xs2));
+    };
+    auto stage_w = [&](int kt) {
+        return kStages == 2 ? ((kt & 1) ? ws1 : ws0) : (kt % 3 == 0 ? ws0 : (kt % 3 == 1 ? ws1 : ws2));
+    };
     // Copy c (0 <= c < kCopies) of K step kt: the X copies first, then the W copies.  A stage's
     // copies go out in two parts, A = [0, kCopies / 2) and B = [kCopies / 2, kCopies).
     constexpr int kPartA = kCopies / 2;
     auto copy = [&](int c, int kt, const uint8_t* lx, const uint8_t* lw, bool plain) {
         const int64_t k0 = static_cast<int64_t>(kt) * kBK;
-        if (c < CopyPlan<kBM>::kPerWave) cx.one(c, xtile + k0, lx, wave, plain, K - k0);
-        else cw.one(c - CopyPlan<kBM>::kPerWave, wtile + k0, lw, wave, plain, K - k0);
+        if (c < CopyX::kPerWave) cx.one(c, xtile + k0, lx, wave, plain, K - k0);
+        else cw.one(c - CopyX::kPerWave, wtile + k0, lw, wave, plain, K - k0);
     };
     auto copies = [&](int c0, int c1, int kt) {      // part of K step kt, any kt < nk
         const bool plain = !(ragged_k && kt == nk - 1);
@@ -381,8 +395,8 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
             for (int c = 0; c < kPartA; ++c)
                 if (c * kMmas / kPartA == q) {
                     const int cc = c0 + c;
-                    if (cc < CopyPlan<kBM>::kPerWave) cx.one(cc, xtile + k0, cxl, wave, true, 0);
-                    else cw.one(cc - CopyPlan<kBM>::kPerWave, wtile + k0, cwl, wave, true, 0);
+                    if (cc < CopyX::kPerWave) cx.one(cc, xtile + k0, cxl, wave, true, 0);
+                    else cw.one(cc - CopyX::kPerWave, wtile + k0, cwl, wave, true, 0);
                 }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -418,24 +432,84 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         for (int q = 0; q < kMmas; ++q) mma_one(f1, q);
     };
 
-    // Prologue: K steps 0 and 1 whole and part A of K step 2; wait for step 0.
-    copies(0, kCopies, 0);
-    if (nk > 1) copies(0, kCopies, 1);
-    if (nk > 2) copies(0, kPartA, 2);
-    if (nk > 2) wait_copies<kCopies + kPartA>();
-    else if (nk > 1) wait_copies<kCopies>();
-    else wait_copies<0>();
-    block_barrier();
-    for (int r = 0; r < kReads; ++r) read_one(f0, xs0, ws0, 0, r);
-    // K steps that need no zero fill: all of them, or all but a ragged last one.
-    const int n_plain = ragged_k ? nk - 1 : nk;
-    int kt = 0;
-    for (; kt + 5 < n_plain; kt += 3) {      // steps kt .. kt + 2 copy plain K steps up to kt + 5
-        full_step(kt, xs0, ws0, xs1, ws1, xs2, ws2);
-        full_step(kt + 1, xs1, ws1, xs2, ws2, xs0, ws0);
-        full_step(kt + 2, xs2, ws2, xs0, ws0, xs1, ws1);
+    const int n_plain = ragged_k ? nk - 1 : nk;     // K steps that need no zero fill
+    if constexpr (kStages == 3) {
+        // Prologue: K steps 0 and 1 whole and part A of K step 2; wait for step 0.
+        copies(0, kCopies, 0);
+        if (nk > 1) copies(0, kCopies, 1);
+        if (nk > 2) copies(0, kPartA, 2);
+        if (nk > 2) wait_copies<kCopies + kPartA>();
+        else if (nk > 1) wait_copies<kCopies>();
+        else wait_copies<0>();
+        block_barrier();
+        for (int r = 0; r < kReads; ++r) read_one(f0, xs0, ws0, 0, r);
+        int kt = 0;
+        for (; kt + 5 < n_plain; kt += 3) {      // steps kt .. kt + 2 copy plain K steps up to kt + 5
+            full_step(kt, xs0, ws0, xs1, ws1, xs2, ws2);
+            full_step(kt + 1, xs1, ws1, xs2, ws2, xs0, ws0);
+            full_step(kt + 2, xs2, ws2, xs0, ws0, xs1, ws1);
+        }
+        for (; kt < nk; ++kt) step(kt);          // the last (at most five) steps
+    } else {
+        // Two stages (for tiles whose three stages would not fit in LDS).  K step kt:
+        //   first half:  matrix cores on f0 (half 0 of stage kt) | read f1 (half 1 of stage kt)
+        //   wait for this wave's copies of kt + 1 and for its fragment reads; the block meets
+        //   second half: matrix cores on f1 | read f0 (half 0 of stage kt + 1) | copy K step kt + 2
+        //                into the stage of kt, which nobody reads any more
+        // so a copy has about one K step to land.  (Issuing the copies in a burst early in the
+        // half-step is slower: with one wave per SIMD, a stalled copy issue idles the matrix core.)
+        auto half2 = [&](const Frags& cur, Frags& nxt, const uint8_t* lx, const uint8_t* lw, int half, int ckt,
+                         const uint8_t* cxl, const uint8_t* cwl, bool with_copies) {
+            const int64_t k0 = static_cast<int64_t>(ckt) * kBK;
+#pragma unroll
+            for (int q = 0; q < kMmas; ++q) {
+                mma_one(cur, q);
+#pragma unroll
+                for (int r = 0; r < kReads; ++r)
+                    if (r * kMmas / kReads == q) read_one(nxt, lx, lw, half, r);
+                if (with_copies) {
+#pragma unroll
+                    for (int c = 0; c < kCopies; ++c)
+                        if (c * kMmas / kCopies == q) {
+                            if (c < CopyX::kPerWave) cx.one(c, xtile + k0, cxl, wave, true, 0);
+                            else cw.one(c - CopyX::kPerWave, wtile + k0, cwl, wave, true, 0);
+                        }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        auto full2 = [&](int kt, const uint8_t* lx, const uint8_t* lw, const uint8_t* nx, const uint8_t* nw) {
+            half2(f0, f1, lx, lw, 1, 0, nullptr, nullptr, false);
+            wait_lds_reads();
+            wait_copies<0>();
+            block_barrier();
+            half2(f1, f0, nx, nw, 0, kt + 2, lx, lw, true);
+        };
+        auto step2 = [&](int kt) {
+            for (int r = 0; r < kReads; ++r) read_one(f1, stage_x(kt), stage_w(kt), 1, r);
+            for (int q = 0; q < kMmas; ++q) mma_one(f0, q);
+            wait_lds_reads();
+            if (kt + 1 < nk) {
+                wait_copies<0>();
+                block_barrier();
+                if (kt + 2 < nk) copies(0, kCopies, kt + 2);
+                for (int r = 0; r < kReads; ++r) read_one(f0, stage_x(kt + 1), stage_w(kt + 1), 0, r);
+            }
+            for (int q = 0; q < kMmas; ++q) mma_one(f1, q);
+        };
+        copies(0, kCopies, 0);
+        if (nk > 1) copies(0, kCopies, 1);
+        if (nk > 1) wait_copies<kCopies>();
+        else wait_copies<0>();
+        block_barrier();
+        for (int r = 0; r < kReads; ++r) read_one(f0, xs0, ws0, 0, r);
+        int kt = 0;
+        for (; kt + 3 < n_plain; kt += 2) {      // steps kt, kt + 1 copy plain K steps kt + 2, kt + 3
+            full2(kt, xs0, ws0, xs1, ws1);
+            full2(kt + 1, xs1, ws1, xs0, ws0);
+        }
+        for (; kt < nk; ++kt) step2(kt);
     }
-    for (; kt < nk; ++kt) step(kt);          // the last (at most five) steps
 
     if constexpr (kOutAcc) {
 #pragma unroll
@@ -447,6 +521,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     } else {
         // Dequantize in registers, stage the wave's kWM x kWN bf16 tile in LDS (rows padded to
         // kOutStride bytes), and write it back as 16-byte pieces of whole output rows.
+        if constexpr (!kPreloadScales) load_scales();
         block_barrier();                 // every wave has finished reading the stages
         uint8_t* const ot = smem + wave * (kWM * kOutStride);
 #pragma unroll
@@ -586,12 +661,25 @@ hipError_t gemm_dispatch(const uint8_t* xq, const float* x_scale, const uint8_t*
                                w_scale, M, N, K, y, out_acc);
         return hipGetLastError();
     }
-    constexpr int kBM = 256, kBN = 128;
-    const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
-    const int tiles_n = static_cast<int>((N + kBN - 1) / kBN);
     const int group_m = 4;
-    hipLaunchKernelGGL((gemm_tile_kernel<kBM, kBN, MT, kOutAcc>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, st,
-                       xq, x_scale, wq, w_scale, M, N, K, y, out_acc, tiles_m, tiles_n, group_m);
+    const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    if (big_tiles >= 512) {
+        // Enough 256 x 256 tiles for two rounds over 256 CUs: 4 waves of 128 x 128 outputs, half the
+        // LDS reads and two thirds of the copies per matrix-core instruction of the smaller tile.
+        constexpr int kBM = 256, kBN = 256, kGM = 2, kGN = 2;
+        const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
+        const int tiles_n = static_cast<int>((N + kBN - 1) / kBN);
+        hipLaunchKernelGGL((gemm_tile_kernel<kBM, kBN, kGM, kGN, 2, MT, kOutAcc>), dim3(tiles_m * tiles_n),
+                           dim3(kGM * kGN * kWave), 0, st, xq, x_scale, wq, w_scale, M, N, K, y, out_acc, tiles_m,
+                           tiles_n, group_m);
+    } else {
+        constexpr int kBM = 256, kBN = 128, kGM = 4, kGN = 2;
+        const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
+        const int tiles_n = static_cast<int>((N + kBN - 1) / kBN);
+        hipLaunchKernelGGL((gemm_tile_kernel<kBM, kBN, kGM, kGN, 3, MT, kOutAcc>), dim3(tiles_m * tiles_n),
+                           dim3(kGM * kGN * kWave), 0, st, xq, x_scale, wq, w_scale, M, N, K, y, out_acc, tiles_m,
+                           tiles_n, group_m);
+    }
     return hipGetLastError();
 }
 

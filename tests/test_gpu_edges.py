@@ -76,6 +76,39 @@ def test_shapes_bf16(f, M, K, N, qtype):
     check_layer(run_layer(f, X, W, qtype=qtype), X, W, qtype=qtype)
 
 
+@pytest.mark.parametrize("qtype,M,K,N", [("int8", 5000, 1040, 6600), ("fp8", 4800, 1168, 6808)])
+def test_big_tile_shapes(f, qtype, M, K, N):
+    """Shapes with at least 512 tiles of 256 x 256 outputs take the two-stage 256 x 256 kernel: ragged
+    M, N and K (a partial last K step) with several steady-state K steps.  Codes and scales in full;
+    accumulators (INT8) and outputs on 64 sampled rows, including the first and the last."""
+    announce(f"big tiles M={M} K={K} N={N} {qtype}")
+    X = synth.random_matrix((M, K), seed=M + K, dtype="bf16", outliers=max(1, K // 100))
+    W = synth.random_matrix((K, N), seed=N + K, dtype="bf16", scale=0.02)
+    x, w = dev(X), dev(W)
+    ax, aw, s = f.w8a8_smooth_scales(x, w, 0.5)
+    wq, sw = f.w8a8_fold_quant_weight(w, s, qtype)
+    xq, sx = f.w8a8_quant_act(x, s, qtype)
+    y = f.w8a8_gemm_dequant(xq, sx, wq, sw, qtype)
+    acc = f.w8a8_gemm_i32(xq, wq) if qtype == "int8" else None
+    torch.cuda.synchronize()
+    _, _, s_ref = oracle.smooth_scales(X, W, 0.5)
+    np.testing.assert_array_equal(host(s), s_ref)
+    qx, sx_ref = oracle.quant_act(X, s_ref, qtype)
+    qw, sw_ref = oracle.fold_quant_weight(W, s_ref, qtype)
+    np.testing.assert_array_equal(host(xq).view(np.uint8), qx.view(np.uint8))
+    np.testing.assert_array_equal(host(wq).view(np.uint8), qw.view(np.uint8))
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.Generator(np.random.PCG64(K)).choice(M, 62, replace=False)]))
+    yg = host(y)[rows]
+    if qtype == "int8":
+        a = oracle.gemm_i32(qx[rows], qw)
+        np.testing.assert_array_equal(host(acc)[rows], a)
+        y64, yb = oracle.dequant_i32(a, sx_ref[rows], sw_ref)
+        np.testing.assert_array_equal(yg, yb)
+    else:
+        y64, mag = oracle.gemm_fp8(qx[rows], qw, sx_ref[rows], sw_ref)
+        assert_rel_tol(yg, y64, 1e-2, extra=fp8_accumulation_bound(K, mag))
+
+
 @pytest.mark.parametrize("M,K,N", [(3, 32, 5), (40, 512, 64), (129, 272, 203)])
 def test_shapes_f32(f, M, K, N):
     announce(f"shape M={M} K={K} N={N} f32")
