@@ -23,7 +23,8 @@
  *   - the rounding of quantize() is round-half-to-even; INT8 codes are clamped to [-127, 127];
  *   - X gets one scale per row (token), W~ one scale per output channel (column of W [K, N]);
  *   - "channel j" of s_j is the contraction index: column j of X, row j of W [K, N];
- *   - a zero maximum gives s_j = 1, and an all-zero row/column gets scale 0 and codes 0;
+ *   - a zero maximum gives s_j = 1; a row/column with scale 0 (all zero, or a maximum whose
+ *     quotient by 127 or 448 underflows) gets codes 0;
  *   - alpha = 0.5 is evaluated as sqrtf(ax) / sqrtf(aw) (two correctly rounded roots and one
  *     division); other alpha use pow in double, rounded once to float;
  *   - dequantize is y = ((float)acc * sx[m]) * sw[n], rounded to bf16 (nearest even); the
@@ -164,7 +165,8 @@ uint8_t oracle_e4m3_encode(float v) {
  * Symmetric quantization of each row of a float32 matrix V [R, C] with one scale per row:
  *   INT8 ([WAQ] s2):  scale = max|v| / 127,  q = clamp(round_half_even(v / scale), -127, 127)
  *   E4M3 ([WAQ] s4):  scale = max|v| / 448,  q = e4m3(clamp(v / scale, -448, 448))
- * A row whose maximum is zero gets scale 0 and all-zero codes.  Codes are stored as bytes.
+ * A row whose scale is zero (its maximum is zero, or so small that max / Q rounds to zero) gets
+ * all-zero codes: v / scale is not defined there.  Codes are stored as bytes.
  * ------------------------------------------------------------------------------------------- */
 void oracle_quantize_rows(const float* v, int64_t R, int64_t C, int qtype, uint8_t* q, float* scale) {
     const float qmax = (qtype == ORACLE_INT8) ? 127.0f : 448.0f;
@@ -177,7 +179,7 @@ void oracle_quantize_rows(const float* v, int64_t R, int64_t C, int qtype, uint8
         scale[r] = sc;
         for (int64_t c = 0; c < C; ++c) {
             uint8_t code;
-            if (amax == 0.0f) {
+            if (sc == 0.0f) {
                 code = 0;
             } else if (qtype == ORACLE_INT8) {
                 float t = nearbyintf(row[c] / sc);

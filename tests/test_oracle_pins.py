@@ -156,6 +156,25 @@ def test_quantize_invariants():
     assert np.all(np.abs(q.astype(np.int32)) <= 127)
 
 
+def test_zero_scale_rows_get_zero_codes():
+    """v / scale is undefined when the scale is 0.  Reading: such a row gets all-zero codes.  That
+    covers an all-zero row and a row whose maximum is so small (a subnormal) that max / Q rounds to
+    0 in float32 -- for Q = 127 and for Q = 448 -- while a slightly larger subnormal maximum gives a
+    nonzero (subnormal) scale and ordinary codes."""
+    tiny = np.float32(1e-44)                     # 1e-44 / 127 and 1e-44 / 448 round to 0
+    assert np.float32(tiny / np.float32(127)) == 0 and np.float32(tiny / np.float32(448)) == 0
+    big = np.float32(2e-43)                      # 2e-43 / 127 is a nonzero subnormal
+    assert np.float32(big / np.float32(127)) > 0
+    X = np.zeros((3, 16), np.float32)
+    X[1, :3] = [tiny, -tiny, np.float32(0.5) * tiny]
+    X[2, :3] = [big, -big, np.float32(0.0)]
+    for qt in ("int8", "fp8_e4m3"):
+        q, sc = oracle.quantize_rows(X, qt)
+        assert sc[0] == 0 and sc[1] == 0 and np.all(q[:2] == 0)
+    q, sc = oracle.quantize_rows(X, "int8")
+    assert sc[2] == np.float32(big / np.float32(127)) and q[2, 0] == 127 and q[2, 1] == -127
+
+
 # ---------------------------------------------------------------------------------------------
 # Smoothing factors: closed forms (s3 "Choosing the Smoothing Factor")
 # ---------------------------------------------------------------------------------------------
