@@ -43,7 +43,7 @@ W8A8_API w8a8_status w8a8_smooth_scales(const void* x, w8a8_dtype x_dtype, int64
     if (!aligned16(x) || !aligned16(w) || !aligned16(ax) || !aligned16(aw) || !aligned16(s)) return W8A8_ERR_UNSUPPORTED;
     hipError_t e = hipSuccess;
     if (!accumulate) e = w8a8::launch_fill(ax, K, 0.0f, stream);
-    if (e == hipSuccess) e = w8a8::launch_absmax_cols(x, x_dtype == W8A8_BF16, M, K, nullptr, ax, stream);
+    if (e == hipSuccess) e = w8a8::launch_absmax_cols(x, x_dtype == W8A8_BF16, M, K, nullptr, 0.0f, ax, stream);
     if (e == hipSuccess) {
         if (N > 0) {
             // row maxima of W and, fused, the smoothing factors from the finished ax
@@ -65,12 +65,11 @@ W8A8_API w8a8_status w8a8_fold_quant_weight(const void* w, w8a8_dtype w_dtype, i
     if (N == 0) return W8A8_OK;
     if (!aligned16(w) || !aligned16(s) || !aligned16(wq) || !aligned16(w_scale)) return W8A8_ERR_UNSUPPORTED;
     const bool bf16 = w_dtype == W8A8_BF16, fp8 = qtype == W8A8_FP8_E4M3;
-    // w_scale holds the column maxima of W~ until the codes are written, then the scales.
+    // The column pass leaves the scales max_j |W~[j, n]| / Q in w_scale; the codes use them.
     hipError_t e = w8a8::launch_fill(w_scale, N, 0.0f, stream);
-    if (e == hipSuccess) e = w8a8::launch_absmax_cols(w, bf16, K, N, s, w_scale, stream);
+    if (e == hipSuccess) e = w8a8::launch_absmax_cols(w, bf16, K, N, s, fp8 ? 448.0f : 127.0f, w_scale, stream);
     if (e == hipSuccess)
         e = w8a8::launch_quant_weight_t(w, bf16, K, N, s, w_scale, fp8, static_cast<uint8_t*>(wq), stream);
-    if (e == hipSuccess) e = w8a8::launch_finalize_scales(w_scale, N, fp8, stream);
     return from_hip(e);
 }
 

@@ -42,10 +42,12 @@ __device__ __forceinline__ void load_chunk(const void* base, int64_t row_start, 
 
 // Column maxima of |a[r, c] * row_scale[r]| over a block of kRowsPerBlock rows and 512 columns,
 // merged across waves in LDS and across blocks with an atomic maximum.  Rows past R re-read row
-// R - 1 and columns past C re-read the last chunk: duplicates do not change a maximum.
+// R - 1 and columns past C re-read the last chunk: duplicates do not change a maximum.  With
+// divisor != 0 the block maxima are divided by it before they are merged: correctly rounded
+// division is monotone, so the merged value is the maximum divided by divisor, rounded once.
 template <bool kBf16, bool kVec, bool kScaled>
 __global__ __launch_bounds__(256) void absmax_cols_kernel(const void* __restrict__ a, int64_t R, int64_t C,
-                                                          const float* __restrict__ row_scale,
+                                                          const float* __restrict__ row_scale, float divisor,
                                                           float* __restrict__ out) {
     __shared__ float part[4][kColsPerWave];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -78,6 +80,7 @@ __global__ __launch_bounds__(256) void absmax_cols_kernel(const void* __restrict
         const int64_t col = static_cast<int64_t>(blockIdx.x) * kColsPerWave + i;
         if (col < C) {
             float mv = fmaxf(fmaxf(part[0][i], part[1][i]), fmaxf(part[2][i], part[3][i]));
+            if (divisor != 0.0f) mv = div_rn(mv, divisor);
             atomic_max_nonneg(out + col, mv);
         }
     }
@@ -135,11 +138,14 @@ __global__ void smooth_factors_kernel(const float* __restrict__ ax, const float*
 }
 
 template <bool kBf16, bool kVec>
-void cols_launch(dim3 grid, const void* a, int64_t R, int64_t C, const float* row_scale, float* out, hipStream_t st) {
+void cols_launch(dim3 grid, const void* a, int64_t R, int64_t C, const float* row_scale, float divisor, float* out,
+                 hipStream_t st) {
     if (row_scale)
-        hipLaunchKernelGGL((absmax_cols_kernel<kBf16, kVec, true>), grid, dim3(256), 0, st, a, R, C, row_scale, out);
+        hipLaunchKernelGGL((absmax_cols_kernel<kBf16, kVec, true>), grid, dim3(256), 0, st, a, R, C, row_scale,
+                           divisor, out);
     else
-        hipLaunchKernelGGL((absmax_cols_kernel<kBf16, kVec, false>), grid, dim3(256), 0, st, a, R, C, row_scale, out);
+        hipLaunchKernelGGL((absmax_cols_kernel<kBf16, kVec, false>), grid, dim3(256), 0, st, a, R, C, row_scale,
+                           divisor, out);
 }
 
 }  // namespace
@@ -151,17 +157,17 @@ hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st) {
 }
 
 hipError_t launch_absmax_cols(const void* a, bool bf16, int64_t R, int64_t C, const float* row_scale,
-                              float* out, hipStream_t st) {
+                              float divisor, float* out, hipStream_t st) {
     if (R <= 0 || C <= 0) return hipSuccess;
     dim3 grid(static_cast<unsigned>((C + kColsPerWave - 1) / kColsPerWave),
               static_cast<unsigned>((R + kRowsPerBlock - 1) / kRowsPerBlock));
     const bool vec = (C % 8) == 0;
     if (bf16) {
-        if (vec) cols_launch<true, true>(grid, a, R, C, row_scale, out, st);
-        else cols_launch<true, false>(grid, a, R, C, row_scale, out, st);
+        if (vec) cols_launch<true, true>(grid, a, R, C, row_scale, divisor, out, st);
+        else cols_launch<true, false>(grid, a, R, C, row_scale, divisor, out, st);
     } else {
-        if (vec) cols_launch<false, true>(grid, a, R, C, row_scale, out, st);
-        else cols_launch<false, false>(grid, a, R, C, row_scale, out, st);
+        if (vec) cols_launch<false, true>(grid, a, R, C, row_scale, divisor, out, st);
+        else cols_launch<false, false>(grid, a, R, C, row_scale, divisor, out, st);
     }
     return hipGetLastError();
 }

@@ -593,19 +593,21 @@ __global__ __launch_bounds__(kThreads) void gemm_small_m_kernel(
     for (int i = 0; i < kMT; ++i) acc[i] = MM::zero();
 
     // Steps with all K bytes inside the rows run kU at a time with every load issued before the
-    // matrix-core work, so a wave keeps (1 + kMT) * kChunks * kU 16-byte loads in flight; the
-    // remaining steps (and a partial last one) zero the bytes past K.
+    // matrix-core work, so a wave keeps (1 + kMT) * kChunks * kU 16-byte loads in flight.  Each wave
+    // takes a contiguous range of per_w such steps (consecutive requests to a row stay together);
+    // the remaining steps (and a partial last one) are spread over the waves and zero the bytes past K.
     constexpr int kU = (16 / ((1 + kMT) * MM::kChunks)) > 0 ? 16 / ((1 + kMT) * MM::kChunks) : 1;
     const int64_t nfull = K / MM::kKStep;
     const int64_t nsteps = (K + MM::kKStep - 1) / MM::kKStep;
-    int64_t st0 = wave;
-    for (; st0 + 4 * (kU - 1) < nfull; st0 += 4 * kU) {
+    const int64_t per_w = (nfull / 4 / kU) * kU;
+    int64_t st0 = wave * per_w;
+    for (int64_t it = 0; it < per_w; it += kU, st0 += kU) {
         v4i fw[kU][MM::kChunks], fx[kU][kMT][MM::kChunks];
 #pragma unroll
         for (int u = 0; u < kU; ++u)
 #pragma unroll
             for (int c = 0; c < MM::kChunks; ++c) {
-                const int64_t k = (st0 + 4 * u) * MM::kKStep + (frag_grp * MM::kChunks + c) * 16;
+                const int64_t k = (st0 + u) * MM::kKStep + (frag_grp * MM::kChunks + c) * 16;
                 fw[u][c] = *reinterpret_cast<const v4i*>(wrow + k);
 #pragma unroll
                 for (int i = 0; i < kMT; ++i) fx[u][i][c] = *reinterpret_cast<const v4i*>(xrow[i] + k);
@@ -615,7 +617,7 @@ __global__ __launch_bounds__(kThreads) void gemm_small_m_kernel(
 #pragma unroll
             for (int i = 0; i < kMT; ++i) acc[i] = MM::run(fw[u], fx[u][i], acc[i]);
     }
-    for (int64_t st = st0; st < nsteps; st += 4) {
+    for (int64_t st = 4 * per_w + wave; st < nsteps; st += 4) {
         v4i fw[MM::kChunks], fx[kMT][MM::kChunks];
 #pragma unroll
         for (int c = 0; c < MM::kChunks; ++c) {

@@ -10,13 +10,14 @@ namespace w8a8 {
 // Fill n floats with v (used instead of a memset so the call sequence stays capturable).
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st);
 
-// out[c] = max(out[c], max_r |a[r, c]| * (scale ? scale[r] : 1)) for a row-major [R, C] matrix of
-// float32 or bf16.  Exact; concurrent blocks merge with an order-independent atomic maximum.
+// out[c] = max(out[c], m_c) with m_c = max_r |a[r, c] * (row_scale ? row_scale[r] : 1)| for a
+// row-major [R, C] matrix of float32 or bf16, divided by divisor (rounded once) when divisor != 0.
+// Exact; concurrent blocks merge with an order-independent atomic maximum.
 hipError_t launch_absmax_cols(const void* a, bool bf16, int64_t R, int64_t C, const float* row_scale,
-                              float* out, hipStream_t st);
+                              float divisor, float* out, hipStream_t st);
 
-// out[r] = max_c |a[r, c]| for a row-major [R, C] matrix (one wave per row, no atomics).
-// Row maxima of a [R, C]; with ax != NULL also s[r] = smoothing factor of (ax[r], out[r]).
+// out[r] = max_c |a[r, c]| for a row-major [R, C] matrix (one wave per row, no atomics); with
+// ax != NULL also s[r] = smoothing factor of (ax[r], out[r]).
 hipError_t launch_absmax_rows(const void* a, bool bf16, int64_t R, int64_t C, float* out, const float* ax,
                               float alpha, float* s, hipStream_t st);
 
@@ -28,13 +29,10 @@ hipError_t launch_smooth_factors(const float* ax, const float* aw, int64_t K, fl
 hipError_t launch_quant_act(const void* x, bool bf16, int64_t M, int64_t K, const float* s, bool fp8,
                             uint8_t* xq, float* x_scale, hipStream_t st);
 
-// Quantize W~ = s * W [K, N] with per-column maxima amax [N] (from launch_absmax_cols) and write
-// the codes transposed, wq [N, K].  amax is read, not changed.
+// Quantize W~ = s * W [K, N] with the per-column scales w_scale [N] (from launch_absmax_cols with
+// divisor 127 or 448) and write the codes transposed, wq [N, K].
 hipError_t launch_quant_weight_t(const void* w, bool bf16, int64_t K, int64_t N, const float* s,
-                                 const float* amax, bool fp8, uint8_t* wq, hipStream_t st);
-
-// scale[n] = amax[n] / (fp8 ? 448 : 127), in place.
-hipError_t launch_finalize_scales(float* amax_to_scale, int64_t n, bool fp8, hipStream_t st);
+                                 const float* w_scale, bool fp8, uint8_t* wq, hipStream_t st);
 
 // GEMM over K-contiguous operands xq [M, K] and wq [N, K]:
 //   acc != nullptr: the raw accumulators [M, N] (int32 for INT8, fp32 for E4M3)

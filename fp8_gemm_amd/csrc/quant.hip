@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kActWaves * kWave) void quant_act_kernel(
         const float sc = div_rn(amax, qmax<kFp8>());
         if (lane == 0 && part == 0) scale[row] = sc;
         uint8_t* const qrow = q + row * K;
-        if (amax == 0.0f) {
+        if (sc == 0.0f) {                       // a zero scale gives zero codes
 #pragma unroll
             for (int i = 0; i < kChunks; ++i) {
                 const int64_t c = lane_c + static_cast<int64_t>(kStride) * i;
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256) void quant_act_long_kernel(const void* __restr
     if (lane == 0) scale[row] = sc;
     for (int64_t c = lane; c < nchunk; c += kWave) {
         uint32_t lo = 0, hi = 0;
-        if (amax != 0.0f) {
+        if (sc != 0.0f) {                       // a zero scale gives zero codes
             float v[8];
             load8<kBf16>(x, row * K + c * 8, v);
             if (s) {
@@ -230,9 +230,10 @@ __global__ __launch_bounds__(256) void quant_act_long_kernel(const void* __restr
 // groups x 8 column chunks) fall in 64 different banks; a 16-byte read of 4 consecutive words
 // returns 4 consecutive row groups (the xor only moves whole aligned groups of 8).
 //
-// Codes use div_by_rcp with each column's correctly rounded 1 / scale when every column scale of
-// the block lies in [2^-60, 2^60] (or its maximum is 0: codes 0); then every W~ whose code can be
-// nonzero is at least 2^-70 and its quotient and remainders are normal.  Otherwise the block
+// The column scales max_j |W~[j, n]| / Q are final when this kernel runs (the column pass divides
+// its maxima by Q).  Codes use div_by_rcp with each column's correctly rounded 1 / scale when every
+// column scale of the block lies in [2^-60, 2^60] or is 0 (codes 0); then every W~ whose code can
+// be nonzero is at least 2^-70 and its quotient and remainders are normal.  Otherwise the block
 // divides in full.
 constexpr int kTJ = 256;
 constexpr int kTN = 128;
@@ -270,8 +271,8 @@ __device__ __forceinline__ void load_item(const void* __restrict__ w, int64_t K,
 
 template <bool kBf16, bool kFp8, bool kVec, bool kFast>
 __device__ __forceinline__ void code_item(const WeightItem<kBf16, kVec>& it, const float (&sj)[4],
-                                          const float* col_amax, const float* col_scale, const float* col_rcp,
-                                          int cl0, uint32_t* __restrict__ tile, int g) {
+                                          const float* col_scale, const float* col_rcp, int cl0,
+                                          uint32_t* __restrict__ tile, int g) {
     float v[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -292,7 +293,7 @@ __device__ __forceinline__ void code_item(const WeightItem<kBf16, kVec>& it, con
             const float ws = sj[i] * v[i][e];
             qv[i] = kFast ? div_by_rcp<kFp8>(ws, sc, col_rcp[c]) : div_rn(ws, sc);
         }
-        const uint32_t word = (col_amax[c] != 0.0f) ? pack_codes4<kFp8>(qv[0], qv[1], qv[2], qv[3]) : 0u;
+        const uint32_t word = (sc != 0.0f) ? pack_codes4<kFp8>(qv[0], qv[1], qv[2], qv[3]) : 0u;
         tile[c * kTStride + (g ^ (8 * ((c >> 3) & 7)))] = word;
     }
 }
@@ -300,21 +301,19 @@ __device__ __forceinline__ void code_item(const WeightItem<kBf16, kVec>& it, con
 template <bool kBf16, bool kFp8, bool kVec>
 __global__ __launch_bounds__(256) void quant_weight_t_kernel(const void* __restrict__ w, int64_t K, int64_t N,
                                                              const float* __restrict__ s,
-                                                             const float* __restrict__ amax,
+                                                             const float* __restrict__ w_scale,
                                                              uint8_t* __restrict__ wq) {
     __shared__ uint32_t tile[kTN * kTStride];
-    __shared__ float col_amax[kTN], col_scale[kTN], col_rcp[kTN], row_s[kTJ];
+    __shared__ float col_scale[kTN], col_rcp[kTN], row_s[kTJ];
     const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kTN;
     const int64_t j0 = static_cast<int64_t>(blockIdx.y) * kTJ;
     bool fast = true;
     if (threadIdx.x < kTN) {
         const int64_t n = n0 + threadIdx.x;
-        const float a = (n < N) ? amax[n] : 0.0f;
-        const float sc = div_rn(a, qmax<kFp8>());
-        col_amax[threadIdx.x] = a;
+        const float sc = (n < N) ? w_scale[n] : 0.0f;
         col_scale[threadIdx.x] = sc;
         col_rcp[threadIdx.x] = div_rn(1.0f, sc);
-        fast = a == 0.0f || in_pow2_range<-60, 60>(sc);
+        fast = sc == 0.0f || in_pow2_range<-60, 60>(sc);
     }
     {
         const int64_t j = j0 + threadIdx.x;
@@ -337,8 +336,8 @@ __global__ __launch_bounds__(256) void quant_weight_t_kernel(const void* __restr
         const int b = wave * 4 + it;
         const int cc = cl + 8 * (b >> 3), g = rl + 8 * (b & 7);
         const float sj[4] = {row_s[4 * g], row_s[4 * g + 1], row_s[4 * g + 2], row_s[4 * g + 3]};
-        if (fast) code_item<kBf16, kFp8, kVec, true>(items[it], sj, col_amax, col_scale, col_rcp, 8 * cc, tile, g);
-        else code_item<kBf16, kFp8, kVec, false>(items[it], sj, col_amax, col_scale, col_rcp, 8 * cc, tile, g);
+        if (fast) code_item<kBf16, kFp8, kVec, true>(items[it], sj, col_scale, col_rcp, 8 * cc, tile, g);
+        else code_item<kBf16, kFp8, kVec, false>(items[it], sj, col_scale, col_rcp, 8 * cc, tile, g);
     }
     __syncthreads();
     // Row n0 + c of wq gets 16-byte piece t (tile rows 16 t .. 16 t + 15 = row groups 4 t .. 4 t + 3,
@@ -349,11 +348,6 @@ __global__ __launch_bounds__(256) void quant_weight_t_kernel(const void* __restr
         const uint4 u = *reinterpret_cast<const uint4*>(&tile[c * kTStride + 4 * (t ^ (2 * ((c >> 3) & 7)))]);
         if (n < N && j < K) *reinterpret_cast<uint4*>(wq + n * K + j) = u;   // K % 16 == 0
     }
-}
-
-__global__ void finalize_scales_kernel(float* p, int64_t n, float qm) {
-    int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = div_rn(p[i], qm);
 }
 
 template <bool kBf16, bool kFp8, int kChunks, bool kPair>
@@ -389,11 +383,11 @@ hipError_t quant_act_dispatch(const void* x, int64_t M, int64_t K, const float* 
 }
 
 template <bool kBf16, bool kFp8>
-hipError_t quant_weight_dispatch(const void* w, int64_t K, int64_t N, const float* s, const float* amax,
+hipError_t quant_weight_dispatch(const void* w, int64_t K, int64_t N, const float* s, const float* w_scale,
                                  uint8_t* wq, hipStream_t st) {
     dim3 grid(static_cast<unsigned>((N + kTN - 1) / kTN), static_cast<unsigned>((K + kTJ - 1) / kTJ));
-    if (N % 8 == 0) hipLaunchKernelGGL((quant_weight_t_kernel<kBf16, kFp8, true>), grid, dim3(256), 0, st, w, K, N, s, amax, wq);
-    else hipLaunchKernelGGL((quant_weight_t_kernel<kBf16, kFp8, false>), grid, dim3(256), 0, st, w, K, N, s, amax, wq);
+    if (N % 8 == 0) hipLaunchKernelGGL((quant_weight_t_kernel<kBf16, kFp8, true>), grid, dim3(256), 0, st, w, K, N, s, w_scale, wq);
+    else hipLaunchKernelGGL((quant_weight_t_kernel<kBf16, kFp8, false>), grid, dim3(256), 0, st, w, K, N, s, w_scale, wq);
     return hipGetLastError();
 }
 
@@ -409,19 +403,13 @@ hipError_t launch_quant_act(const void* x, bool bf16, int64_t M, int64_t K, cons
 }
 
 hipError_t launch_quant_weight_t(const void* w, bool bf16, int64_t K, int64_t N, const float* s,
-                                 const float* amax, bool fp8, uint8_t* wq, hipStream_t st) {
+                                 const float* w_scale, bool fp8, uint8_t* wq, hipStream_t st) {
     if (N <= 0) return hipSuccess;
-    if (bf16) return fp8 ? quant_weight_dispatch<true, true>(w, K, N, s, amax, wq, st)
-                         : quant_weight_dispatch<true, false>(w, K, N, s, amax, wq, st);
-    return fp8 ? quant_weight_dispatch<false, true>(w, K, N, s, amax, wq, st)
-               : quant_weight_dispatch<false, false>(w, K, N, s, amax, wq, st);
+    if (bf16) return fp8 ? quant_weight_dispatch<true, true>(w, K, N, s, w_scale, wq, st)
+                         : quant_weight_dispatch<true, false>(w, K, N, s, w_scale, wq, st);
+    return fp8 ? quant_weight_dispatch<false, true>(w, K, N, s, w_scale, wq, st)
+               : quant_weight_dispatch<false, false>(w, K, N, s, w_scale, wq, st);
 }
 
-hipError_t launch_finalize_scales(float* p, int64_t n, bool fp8, hipStream_t st) {
-    if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(finalize_scales_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
-                       p, n, fp8 ? 448.0f : 127.0f);
-    return hipGetLastError();
-}
 
 }  // namespace w8a8

@@ -31,8 +31,9 @@
  *     W8A8_ERR_INVALID_ARG, checked before anything is queued; a failed launch -> W8A8_ERR_HIP.
  *   - Arithmetic: divisions are IEEE fp32 divisions and roundings are to nearest, ties to even,
  *     so the quantized codes, scales and int32 accumulators are deterministic and reproducible
- *     bit for bit.  A zero maximum gives s_j = 1; an all-zero row or column gets scale 0 and
- *     codes 0.  NaN and infinite inputs are not supported.
+ *     bit for bit.  A zero maximum gives s_j = 1; a row or column whose scale is 0 (all zero, or a
+ *     maximum so small that its quotient by 127 or 448 rounds to 0) gets codes 0.  NaN and
+ *     infinite inputs are not supported, nor are X / s or s * W that overflow.
  */
 #ifndef W8A8_H
 #define W8A8_H
@@ -78,7 +79,7 @@ w8a8_status w8a8_smooth_scales(const void* x, w8a8_dtype x_dtype, int64_t M, int
  *   wq[n, j]   = INT8: clamp(round_half_even(W~[j, n] / w_scale[n]), -127, 127)
  *                E4M3: e4m3_round_half_even(clamp(W~[j, n] / w_scale[n], -448, 448))
  * w: [K, N] in w_dtype.  s: fp32 [K] or NULL.  wq: [N, K] bytes (written).  w_scale: fp32 [N]
- * (written; also used as scratch while the call runs).
+ * (written; it accumulates the column maxima while the call runs).
  */
 w8a8_status w8a8_fold_quant_weight(const void* w, w8a8_dtype w_dtype, int64_t K, int64_t N,
                                    const float* s, w8a8_qtype qtype, void* wq, float* w_scale,

@@ -144,6 +144,33 @@ def test_zero_rows_and_columns(f):
         assert g["s"][9] == 1 and g["s"][30] == 1
 
 
+def test_underflowing_scales(f):
+    """A token row or an output column whose maximum is so small that max / Q rounds to 0 gets
+    scale 0 and codes 0, like an all-zero one; a slightly larger subnormal maximum gives a subnormal
+    scale and ordinary codes."""
+    announce("underflowing scales")
+    M, K, N = 12, 64, 24
+    X = synth.random_matrix((M, K), seed=33, outliers=2)
+    W = synth.random_matrix((K, N), seed=34, scale=0.02)
+    X[3] = 0.0
+    X[3, :3] = np.float32([1e-44, -1e-44, 5e-45])
+    X[5] = 0.0
+    X[5, :2] = np.float32([2e-43, -2e-43])
+    W[:, 7] = 0.0
+    W[:4, 7] = np.float32([1e-44, -1e-44, 0.0, 3e-45])
+    for q in ("int8", "fp8"):
+        xq, sx = f.w8a8_quant_act(dev(X), None, q)
+        wq, sw = f.w8a8_fold_quant_weight(dev(W), None, q)
+        torch.cuda.synchronize()
+        qx_ref, sx_ref = oracle.quant_act(X, None, q)
+        qw_ref, sw_ref = oracle.fold_quant_weight(W, None, q)
+        np.testing.assert_array_equal(host(sx), sx_ref)
+        np.testing.assert_array_equal(host(xq).view(np.uint8), qx_ref.view(np.uint8))
+        np.testing.assert_array_equal(host(sw), sw_ref)
+        np.testing.assert_array_equal(host(wq).view(np.uint8), qw_ref.view(np.uint8))
+        assert sx_ref[3] == 0 and sw_ref[7] == 0 and (sx_ref[5] > 0) == (q == "int8")
+
+
 def test_no_smoothing_and_ties(f):
     """s = NULL (no smoothing); rows whose max is 127 (scale exactly 1) put x / scale on .5 ties."""
     announce("ties without smoothing")
