@@ -257,9 +257,9 @@ __device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_m,
     tn = in / gm;
 }
 
-template <int kBM, int kBN, int kGM, int kGN, int kStages, typename MM, bool kOutAcc>
+template <int kBM, int kBN, int kGM, int kGN, int kStages, int kWavesPerSimd, typename MM, bool kOutAcc>
 __global__ __launch_bounds__(kGM * kGN * kWave, 1)
-__attribute__((amdgpu_waves_per_eu(kGM * kGN / 4, kGM * kGN / 4))) void gemm_tile_kernel(
+__attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void gemm_tile_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ x_scale, const uint8_t* __restrict__ wq,
     const float* __restrict__ w_scale, int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y,
     void* __restrict__ out_acc, int tiles_m, int tiles_n, int group_m) {
@@ -647,9 +647,86 @@ __global__ __launch_bounds__(kThreads) void gemm_small_m_kernel(
     }
 }
 
+// ------------------------------------------------------------------------------------------------
+// Decode kernel (M <= 16, K = 4 * kS * kKStep): bound by reading W once.  Each of the 4 waves of a
+// block owns a contiguous quarter of K and holds its X fragments for that quarter in registers for
+// the whole kernel, so X is read once per wave instead of once per output tile.  A block walks the
+// 16-column output tiles t = blockIdx.x, blockIdx.x + gridDim.x, ...: it loads the W fragments of
+// the next tile while the matrix cores work on the current one, then adds the 4 partial sums in LDS
+// (exact for INT8) and the first wave stores them.
+// ------------------------------------------------------------------------------------------------
+template <int kS, typename MM, bool kOutAcc>
+__global__ __launch_bounds__(kThreads) void gemm_decode_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ x_scale, const uint8_t* __restrict__ wq,
+    const float* __restrict__ w_scale, int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y,
+    void* __restrict__ out_acc) {
+    using Acc = typename MM::Acc;
+    static_assert(MM::kTile == 16, "16x16 blocks");
+    constexpr int kC = MM::kChunks;
+    __shared__ Acc red[3][kWave];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int frag_row = lane & 15, frag_grp = lane >> 4;
+    const int64_t kw0 = static_cast<int64_t>(wave) * kS * MM::kKStep;   // this wave's quarter of K
+    const int ntiles = static_cast<int>((N + 15) / 16);
+    const int G = static_cast<int>(gridDim.x);
+
+    v4i fx[kS][kC];
+    {
+        const int64_t m = frag_row < M ? frag_row : M - 1;
+        const uint8_t* xr = xq + m * K + kw0;
+#pragma unroll
+        for (int s = 0; s < kS; ++s)
+#pragma unroll
+            for (int c = 0; c < kC; ++c)
+                fx[s][c] = *reinterpret_cast<const v4i*>(xr + s * MM::kKStep + (frag_grp * kC + c) * 16);
+    }
+    v4i fw[2][kS][kC];
+    auto load_w = [&](v4i (&dst)[kS][kC], int t) {
+        int64_t n = static_cast<int64_t>(t) * 16 + frag_row;
+        n = n < N ? n : N - 1;
+        const uint8_t* wr = wq + n * K + kw0;
+#pragma unroll
+        for (int s = 0; s < kS; ++s)
+#pragma unroll
+            for (int c = 0; c < kC; ++c)
+                dst[s][c] = *reinterpret_cast<const v4i*>(wr + s * MM::kKStep + (frag_grp * kC + c) * 16);
+    };
+    // Tile t with its W fragments in cur; the next tile's go into nxt first.
+    auto tile_step = [&](const v4i (&cur)[kS][kC], v4i (&nxt)[kS][kC], int t) {
+        if (t + G < ntiles) load_w(nxt, t + G);
+        Acc acc = MM::zero();
+#pragma unroll
+        for (int s = 0; s < kS; ++s) acc = MM::run(cur[s], fx[s], acc);
+        if (wave > 0) red[wave - 1][lane] = acc;
+        __syncthreads();
+        if (wave == 0) {
+            Acc a = acc;
+#pragma unroll
+            for (int w = 0; w < 3; ++w) a += red[w][lane];
+            store_block<MM, kOutAcc>(a, 0, static_cast<int64_t>(t) * 16, lane, M, N, x_scale, w_scale, y, out_acc);
+        }
+        __syncthreads();                 // red is reused by the next tile
+    };
+    int t = blockIdx.x;
+    if (t < ntiles) load_w(fw[0], t);
+    for (; t < ntiles; t += 2 * G) {     // the register buffers alternate with compile-time indices
+        tile_step(fw[0], fw[1], t);
+        if (t + G < ntiles) tile_step(fw[1], fw[0], t + G);
+    }
+}
+
 template <typename M16, typename MT, bool kOutAcc>
 hipError_t gemm_dispatch(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale,
                          int64_t M, int64_t N, int64_t K, uint16_t* y, void* out_acc, hipStream_t st) {
+    if (M <= 16 && K == 4 * 16 * M16::kKStep) {
+        // decode shape: X in registers, persistent grid with an equal number of tiles per block
+        const int64_t ntiles = (N + 15) / 16;
+        const int64_t per_block = (ntiles + 511) / 512;
+        const int64_t grid = (ntiles + per_block - 1) / per_block;
+        hipLaunchKernelGGL((gemm_decode_kernel<16, M16, kOutAcc>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
+                           st, xq, x_scale, wq, w_scale, M, N, K, y, out_acc);
+        return hipGetLastError();
+    }
     if (M <= 64) {
         dim3 grid(static_cast<unsigned>((N + 15) / 16));
         if (M <= 16)
@@ -671,14 +748,14 @@ hipError_t gemm_dispatch(const uint8_t* xq, const float* x_scale, const uint8_t*
         constexpr int kBM = 256, kBN = 256, kGM = 2, kGN = 2;
         const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
         const int tiles_n = static_cast<int>((N + kBN - 1) / kBN);
-        hipLaunchKernelGGL((gemm_tile_kernel<kBM, kBN, kGM, kGN, 2, MT, kOutAcc>), dim3(tiles_m * tiles_n),
+        hipLaunchKernelGGL((gemm_tile_kernel<kBM, kBN, kGM, kGN, 2, 1, MT, kOutAcc>), dim3(tiles_m * tiles_n),
                            dim3(kGM * kGN * kWave), 0, st, xq, x_scale, wq, w_scale, M, N, K, y, out_acc, tiles_m,
                            tiles_n, group_m);
     } else {
         constexpr int kBM = 256, kBN = 128, kGM = 4, kGN = 2;
         const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
         const int tiles_n = static_cast<int>((N + kBN - 1) / kBN);
-        hipLaunchKernelGGL((gemm_tile_kernel<kBM, kBN, kGM, kGN, 3, MT, kOutAcc>), dim3(tiles_m * tiles_n),
+        hipLaunchKernelGGL((gemm_tile_kernel<kBM, kBN, kGM, kGN, 3, 2, MT, kOutAcc>), dim3(tiles_m * tiles_n),
                            dim3(kGM * kGN * kWave), 0, st, xq, x_scale, wq, w_scale, M, N, K, y, out_acc, tiles_m,
                            tiles_n, group_m);
     }

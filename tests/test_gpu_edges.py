@@ -109,6 +109,17 @@ def test_big_tile_shapes(f, qtype, M, K, N):
         assert_rel_tol(yg, y64, 1e-2, extra=fp8_accumulation_bound(K, mag))
 
 
+@pytest.mark.parametrize("qtype,M,K,N", [("int8", 7, 4096, 9600), ("int8", 16, 4096, 1000), ("fp8", 5, 8192, 700)])
+def test_decode_shapes(f, qtype, M, K, N):
+    """Decode-shaped GEMMs (M <= 16 with K = 4096 for INT8, 8192 for E4M3) take the kernel that keeps
+    X in registers and walks several output tiles per block: fewer rows than 16, a ragged last
+    tile, and blocks with one and with two tiles."""
+    announce(f"decode M={M} K={K} N={N} {qtype}")
+    X = synth.random_matrix((M, K), seed=M + N, dtype="bf16", outliers=K // 100)
+    W = synth.random_matrix((K, N), seed=K + N, dtype="bf16", scale=0.02)
+    check_layer(run_layer(f, X, W, qtype=qtype), X, W, qtype=qtype)
+
+
 @pytest.mark.parametrize("M,K,N", [(3, 32, 5), (40, 512, 64), (129, 272, 203)])
 def test_shapes_f32(f, M, K, N):
     announce(f"shape M={M} K={K} N={N} f32")
