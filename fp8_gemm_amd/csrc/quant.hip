@@ -218,8 +218,9 @@ __global__ __launch_bounds__(256) void quant_act_long_kernel(const void* __restr
 
 // ---- weights: W~ = s * W [K, N] -> codes transposed to wq [N, K] --------------------------------
 //
-// A block of 256 threads owns a tile of kTJ = 256 rows (j) x kTN = 128 columns (n) of W.  Loads are
-// coalesced along n: a wave instruction reads 8 rows x 128 bytes.  Each thread handles 8 columns x
+// A block of 256 threads owns a tile of kTJ = 256 rows (j) x kTN = 64 columns (n) of W (small
+// enough for four blocks per CU).  Loads are coalesced along n: a wave instruction reads 8 rows x
+// 128 bytes (bf16).  Each thread handles 8 columns x
 // 4 consecutive rows at a time, forms W~ = s[j] * W[j, n] and the codes with the column scales, and
 // packs the 4 codes of one column (rows j .. j + 3) into one LDS word; the tile is stored transposed,
 // one row of kTJ / 4 words per column n, and written back as 16-byte pieces of wq rows (contiguous
@@ -236,8 +237,10 @@ __global__ __launch_bounds__(256) void quant_act_long_kernel(const void* __restr
 // be nonzero is at least 2^-70 and its quotient and remainders are normal.  Otherwise the block
 // divides in full.
 constexpr int kTJ = 256;
-constexpr int kTN = 128;
+constexpr int kTN = 64;
 constexpr int kTStride = kTJ / 4 + 8;
+constexpr int kItems = (kTJ / 4) * (kTN / 8) / 256;   // (row group, column chunk) items per thread
+static_assert(kItems >= 1 && kTN % 64 == 0, "8 column chunks per wave instruction");
 
 template <bool kBf16>
 __device__ __forceinline__ float load1(const void* base, int64_t i) {
@@ -322,19 +325,20 @@ __global__ __launch_bounds__(256) void quant_weight_t_kernel(const void* __restr
     fast = __syncthreads_and(fast);
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int cl = lane & 7, rl = lane >> 3;
-    // 64 row groups x 16 column chunks, 4 (group, chunk) items per thread.  Item it of wave w is
-    // combination b = 4 w + it: column chunk cc = cl + 8 (b / 8), row group g = rl + 8 (b % 8).
-    WeightItem<kBf16, kVec> items[4];
+    // kTJ / 4 row groups x kTN / 8 column chunks, kItems (group, chunk) items per thread.  Item it of
+    // wave w is combination b = kItems w + it: column chunk cc = cl + 8 (b / (kTJ / 32)), row group
+    // g = rl + 8 (b % (kTJ / 32)).
+    WeightItem<kBf16, kVec> items[kItems];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int b = wave * 4 + it;
-        const int cc = cl + 8 * (b >> 3), g = rl + 8 * (b & 7);
+    for (int it = 0; it < kItems; ++it) {
+        const int b = wave * kItems + it;
+        const int cc = cl + 8 * (b / (kTJ / 32)), g = rl + 8 * (b % (kTJ / 32));
         load_item<kBf16, kVec>(w, K, N, j0 + 4 * g, n0 + 8 * cc, items[it]);
     }
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int b = wave * 4 + it;
-        const int cc = cl + 8 * (b >> 3), g = rl + 8 * (b & 7);
+    for (int it = 0; it < kItems; ++it) {
+        const int b = wave * kItems + it;
+        const int cc = cl + 8 * (b / (kTJ / 32)), g = rl + 8 * (b % (kTJ / 32));
         const float sj[4] = {row_s[4 * g], row_s[4 * g + 1], row_s[4 * g + 2], row_s[4 * g + 3]};
         if (fast) code_item<kBf16, kFp8, kVec, true>(items[it], sj, col_scale, col_rcp, 8 * cc, tile, g);
         else code_item<kBf16, kFp8, kVec, false>(items[it], sj, col_scale, col_rcp, 8 * cc, tile, g);
@@ -375,7 +379,9 @@ hipError_t quant_act_dispatch(const void* x, int64_t M, int64_t K, const float* 
     if (per_lane <= 1) quant_act_launch<kBf16, kFp8, 1, false>(x, M, K, s, xq, xs, st);
     else if (per_lane <= 2) quant_act_launch<kBf16, kFp8, 2, false>(x, M, K, s, xq, xs, st);
     else if (per_lane <= 4) quant_act_launch<kBf16, kFp8, 4, false>(x, M, K, s, xq, xs, st);
-    else if (per_lane <= 8) quant_act_launch<kBf16, kFp8, 8, false>(x, M, K, s, xq, xs, st);
+    // K in (2048, 8192]: two waves per row (more, smaller waves interleave the loads and the
+    // arithmetic of different rows better than one wave holding the whole row).
+    else if (per_lane <= 8) quant_act_launch<kBf16, kFp8, 4, true>(x, M, K, s, xq, xs, st);
     else if (per_lane <= 16) quant_act_launch<kBf16, kFp8, 8, true>(x, M, K, s, xq, xs, st);
     else hipLaunchKernelGGL((quant_act_long_kernel<kBf16, kFp8>), dim3(static_cast<unsigned>((M + 3) / 4)), dim3(256), 0,
                             st, x, s, M, K, xq, xs);
