@@ -85,21 +85,21 @@ __device__ __forceinline__ void store_codes(const float (&v)[kChunks][8], float 
     }
 }
 
-template <bool kBf16, bool kFp8, int kChunks, bool kSmooth, bool kPair>
+template <bool kBf16, bool kFp8, int kChunks, bool kSmooth, int kSplit>
 __global__ __launch_bounds__(kActWaves * kWave) void quant_act_kernel(
     const void* __restrict__ x, const float* __restrict__ s, int64_t M, int64_t K, int rows_per_wave,
     uint8_t* __restrict__ q, float* __restrict__ scale) {
     extern __shared__ float sh[];               // kSmooth: s then 1/s, each K floats (lds_half order)
-    __shared__ float xchg[2][kActWaves];        // kPair: the two halves' maxima of a row
+    __shared__ float xchg[2][kActWaves];        // kSplit > 1: the parts' maxima of a row
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int64_t nchunk = K / 8;
     float* const sh_s = sh;
     float* const sh_r = sh + K;
     bool fast_s = true;
     if constexpr (kSmooth) {
-        // K <= (kPair ? 2 : 1) * kChunks * 512: at most that many elements per thread, loaded
+        // K <= kSplit * kChunks * 512: at most kSplit * kChunks elements per thread, loaded
         // together (indices past K re-read s[K - 1] and are not stored).
-        constexpr int kPer = (kPair ? 2 : 1) * kChunks;
+        constexpr int kPer = kSplit * kChunks;
         float sv[kPer];
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
@@ -118,17 +118,16 @@ __global__ __launch_bounds__(kActWaves * kWave) void quant_act_kernel(
         }
         fast_s = __syncthreads_and(fast_s);
     }
-    // A row is handled by one wave, or (kPair) by the waves 2p and 2p + 1, which take alternate
-    // 512-element blocks of it.
-    constexpr int kRowsPerPass = kPair ? kActWaves / 2 : kActWaves;
-    const int slot = kPair ? wave / 2 : wave;
-    const int part = kPair ? wave % 2 : 0;
+    // A row is handled by kSplit consecutive waves, which take interleaved 512-element blocks of it.
+    constexpr int kRowsPerPass = kActWaves / kSplit;
+    const int slot = wave / kSplit;
+    const int part = wave % kSplit;
     const int lane_c = part * kWave + lane;     // first chunk of this wave's share
-    constexpr int kStride = (kPair ? 2 : 1) * kWave;
+    constexpr int kStride = kSplit * kWave;
     for (int rr = 0; rr < rows_per_wave; ++rr) {
         const int64_t row = (static_cast<int64_t>(blockIdx.x) * rows_per_wave + rr) * kRowsPerPass + slot;
         const bool live = row < M;
-        if (!kPair && !live) break;
+        if (kSplit == 1 && !live) break;
         const int64_t rrow = live ? row : M - 1;
         // All loads unconditional (chunks past the row end re-read the last chunk, which changes
         // no maximum and is never stored) and issued before any conversion, so that they are all
@@ -146,10 +145,11 @@ __global__ __launch_bounds__(kActWaves * kWave) void quant_act_kernel(
         float amax = fast_s ? smooth_chunks<true, kSmooth, kFp8>(v, sh_s, sh_r, lane_c, kStride, nchunk)
                             : smooth_chunks<false, kSmooth, kFp8>(v, sh_s, sh_r, lane_c, kStride, nchunk);
         amax = wave_max(amax);
-        if constexpr (kPair) {
+        if constexpr (kSplit > 1) {
             if (lane == 0) xchg[rr & 1][wave] = amax;
             __syncthreads();
-            amax = fmaxf(amax, xchg[rr & 1][wave ^ 1]);
+#pragma unroll
+            for (int p = 0; p < kSplit; ++p) amax = fmaxf(amax, xchg[rr & 1][slot * kSplit + p]);
         }
         if (!live) continue;
         const float sc = div_rn(amax, qmax<kFp8>());
@@ -354,21 +354,21 @@ __global__ __launch_bounds__(256) void quant_weight_t_kernel(const void* __restr
     }
 }
 
-template <bool kBf16, bool kFp8, int kChunks, bool kPair>
+template <bool kBf16, bool kFp8, int kChunks, int kSplit>
 void quant_act_launch(const void* x, int64_t M, int64_t K, const float* s, uint8_t* xq, float* xs, hipStream_t st) {
     // Rows per wave: one, or more once there are enough rows for two blocks per CU on 256 CUs.
-    const int64_t rows_per_pass = kPair ? kActWaves / 2 : kActWaves;
+    const int64_t rows_per_pass = kActWaves / kSplit;
     const int64_t rows_per_block_pass = rows_per_pass * 512;
     const int rpw = static_cast<int>(std::max<int64_t>(1, (M + rows_per_block_pass - 1) / rows_per_block_pass));
     const int64_t rows_per_block = rows_per_pass * rpw;
     dim3 grid(static_cast<unsigned>((M + rows_per_block - 1) / rows_per_block)), block(kActWaves * kWave);
     if (s) {
         const size_t lds = 2 * static_cast<size_t>(K) * sizeof(float);
-        hipLaunchKernelGGL((quant_act_kernel<kBf16, kFp8, kChunks, true, kPair>), grid, block, lds, st, x, s, M, K, rpw,
-                           xq, xs);
+        hipLaunchKernelGGL((quant_act_kernel<kBf16, kFp8, kChunks, true, kSplit>), grid, block, lds, st, x, s, M, K,
+                           rpw, xq, xs);
     } else {
-        hipLaunchKernelGGL((quant_act_kernel<kBf16, kFp8, kChunks, false, kPair>), grid, block, 0, st, x, s, M, K, rpw,
-                           xq, xs);
+        hipLaunchKernelGGL((quant_act_kernel<kBf16, kFp8, kChunks, false, kSplit>), grid, block, 0, st, x, s, M, K,
+                           rpw, xq, xs);
     }
 }
 
@@ -376,13 +376,13 @@ template <bool kBf16, bool kFp8>
 hipError_t quant_act_dispatch(const void* x, int64_t M, int64_t K, const float* s, uint8_t* xq, float* xs,
                               hipStream_t st) {
     const int64_t per_lane = (K / 8 + kWave - 1) / kWave;
-    if (per_lane <= 1) quant_act_launch<kBf16, kFp8, 1, false>(x, M, K, s, xq, xs, st);
-    else if (per_lane <= 2) quant_act_launch<kBf16, kFp8, 2, false>(x, M, K, s, xq, xs, st);
-    else if (per_lane <= 4) quant_act_launch<kBf16, kFp8, 4, false>(x, M, K, s, xq, xs, st);
-    // K in (2048, 8192]: two waves per row (more, smaller waves interleave the loads and the
-    // arithmetic of different rows better than one wave holding the whole row).
-    else if (per_lane <= 8) quant_act_launch<kBf16, kFp8, 4, true>(x, M, K, s, xq, xs, st);
-    else if (per_lane <= 16) quant_act_launch<kBf16, kFp8, 8, true>(x, M, K, s, xq, xs, st);
+    if (per_lane <= 1) quant_act_launch<kBf16, kFp8, 1, 1>(x, M, K, s, xq, xs, st);
+    else if (per_lane <= 2) quant_act_launch<kBf16, kFp8, 2, 1>(x, M, K, s, xq, xs, st);
+    else if (per_lane <= 4) quant_act_launch<kBf16, kFp8, 4, 1>(x, M, K, s, xq, xs, st);
+    // K in (2048, 8192]: two or four waves per row (more, smaller waves interleave the loads and
+    // the arithmetic of different rows better than one wave holding the whole row).
+    else if (per_lane <= 8) quant_act_launch<kBf16, kFp8, 4, 2>(x, M, K, s, xq, xs, st);
+    else if (per_lane <= 16) quant_act_launch<kBf16, kFp8, 4, 4>(x, M, K, s, xq, xs, st);
     else hipLaunchKernelGGL((quant_act_long_kernel<kBf16, kFp8>), dim3(static_cast<unsigned>((M + 3) / 4)), dim3(256), 0,
                             st, x, s, M, K, xq, xs);
     return hipGetLastError();

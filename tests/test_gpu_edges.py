@@ -64,6 +64,7 @@ SHAPES = [
     # (M, K, N): small-M kernel (1, 2 and 4 row tiles), tiled kernel with ragged M / N / K tails
     (1, 16, 1), (5, 48, 7), (16, 512, 512), (17, 256, 33), (33, 1024, 130), (64, 2048, 96),
     (65, 128, 128), (300, 592, 200), (257, 4096, 129), (512, 1040, 384),
+    (70, 6160, 96),     # activation rows of 4097..8192 elements: four waves per row, ragged chunks
 ]
 
 
