@@ -53,6 +53,10 @@ def _load():
         "oracle_bf16_rne": (ctypes.c_uint16, [F]),
         "oracle_dequant_i32": (None, [P, P, P, I64, I64, P, P]),
         "oracle_gemm_fp8": (I, [P, P, I64, I64, I64, P, P, P, P]),
+        "oracle_absmax_tensor": (F, [P, I, I64]),
+        "oracle_tensor_scale": (F, [F, I]),
+        "oracle_quantize_tensor": (None, [P, I, I64, F, I, P]),
+        "oracle_quant_weight_tensor": (I, [P, I, I64, I64, I, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -273,5 +277,66 @@ def layer(x, w, alpha=0.5, qtype="int8"):
         out.update(acc=acc, y64=y64, y_bf16=yb)
     else:
         y64, mag = gemm_fp8(qx, qw, sx, sw)
+        out.update(y64=y64, mag64=mag)
+    return out
+
+
+# --- per-tensor scaling (Weight-Activation Quantization, s4 "Per-Tensor Scaling for FP8"; s2) --
+
+def absmax_tensor(a) -> np.float32:
+    """max |a| over the whole tensor."""
+    a, dt = _input(a)
+    return np.float32(_load().oracle_absmax_tensor(_ptr(a), dt, a.size))
+
+
+def tensor_scale(amax, qtype="fp8") -> np.float32:
+    """s = amax / Q (127 for INT8, 448 for E4M3), one fp32 division."""
+    return np.float32(_load().oracle_tensor_scale(float(np.float32(amax)), qtype_code(qtype)))
+
+
+def quant_tensor(a, amax, qtype="fp8"):
+    """Codes of a / s with the one scale s = amax / Q, saturating at +-Q (amax may be an earlier
+    tensor's maximum: delayed scaling).  Returns (codes shaped like a, s)."""
+    lib = _load()
+    q = qtype_code(qtype)
+    a, dt = _input(a)
+    sc = tensor_scale(amax, q)
+    codes = np.empty(a.shape, np.uint8)
+    lib.oracle_quantize_tensor(_ptr(a), dt, a.size, float(sc), q, _ptr(codes))
+    return _codes(codes, q), sc
+
+
+def quant_weight_tensor(w, qtype="fp8"):
+    """W [K, N] -> (codes [N, K], the one scale max|W| / Q)."""
+    lib = _load()
+    q = qtype_code(qtype)
+    w, dt = _input(w)
+    K, N = w.shape
+    codes = np.empty((N, K), np.uint8)
+    sc = np.empty(1, np.float32)
+    if lib.oracle_quant_weight_tensor(_ptr(w), dt, K, N, q, _ptr(codes), _ptr(sc)) != 0:
+        raise MemoryError("oracle_quant_weight_tensor")
+    return _codes(codes, q), sc[0]
+
+
+def layer_tensor(x, w, qtype="fp8", amax_x=None):
+    """The per-tensor path of s4 on the CPU: one scale for W, one for X, no smoothing.
+
+    amax_x: the maximum X's scale is taken from; None takes this X's own maximum (current
+    scaling), a number an earlier step's (delayed scaling, values beyond it saturate).
+    """
+    q = qtype_code(qtype)
+    qw, sw = quant_weight_tensor(w, q)
+    amax_now = absmax_tensor(x)
+    qx, sx = quant_tensor(x, amax_now if amax_x is None else amax_x, q)
+    M, N = x.shape[0], w.shape[1]
+    sxv, swv = np.full(M, sx, np.float32), np.full(N, sw, np.float32)
+    out = dict(qw=qw, sw=sw, qx=qx, sx=sx, amax_x=amax_now)
+    if q == INT8:
+        acc = gemm_i32(qx, qw)
+        y64, yb = dequant_i32(acc, sxv, swv)
+        out.update(acc=acc, y64=y64, y_bf16=yb)
+    else:
+        y64, mag = gemm_fp8(qx, qw, sxv, swv)
         out.update(y64=y64, mag64=mag)
     return out

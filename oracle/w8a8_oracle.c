@@ -30,7 +30,9 @@
  *   - dequantize is y = ((float)acc * sx[m]) * sw[n], rounded to bf16 (nearest even); the
  *     reference value y64 = acc * sx * sw is also returned in double;
  *   - E4M3 is the OCP "fn" flavour: bias 7, largest finite 448, subnormals m * 2^-9, no
- *     infinities; values are clamped to [-448, 448] before rounding.
+ *     infinities; values are clamped to [-448, 448] before rounding;
+ *   - per-tensor scaling (s4) uses one scale max|x| / Q for a whole tensor, without smoothing;
+ *     under delayed scaling the maximum is an earlier tensor's, and values beyond Q * s saturate.
  *
  * Arithmetic: IEEE binary32/binary64, round-to-nearest-even, compiled without fast-math and
  * without FMA contraction.  Every loop is the definition written out; the only parallelism is an
@@ -307,5 +309,66 @@ int oracle_gemm_fp8(const uint8_t* qx, const uint8_t* qw, int64_t M, int64_t N, 
             if (mag64) mag64[m * N + n] = ldexp((double)u, -18) * scale;
         }
     }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Per-tensor scaling ([WAQ] s4 "Per-Tensor Scaling for FP8": q = cast_fp8(x / s), x^ = s q with
+ * s = max|x| / 448; [WAQ] s2 gives the same per-tensor recipe for INT8 with 127).  One scale
+ * serves a whole tensor.  Under delayed scaling ([WAQ] s4, the FP8-vs-INT8 table: the scale comes
+ * from the previous step's maximum) the maximum is an earlier tensor's, so values beyond Q * s
+ * occur; x / s is clamped to [-Q, Q] before rounding, i.e. they saturate.
+ * ------------------------------------------------------------------------------------------- */
+
+/* max |a[i]| over n elements (float32 or bf16). */
+float oracle_absmax_tensor(const void* a, int dtype, int64_t n) {
+    float amax = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        const float v = fabsf(load_elem(a, dtype, i));
+        if (v > amax) amax = v;
+    }
+    return amax;
+}
+
+/* s = amax / Q (Q = 127 for INT8, 448 for E4M3), one IEEE fp32 division. */
+float oracle_tensor_scale(float amax, int qtype) {
+    return amax / ((qtype == ORACLE_INT8) ? 127.0f : 448.0f);
+}
+
+/* q[i] = code(clamp(a[i] / scale, -Q, Q)) for n elements; scale 0 gives codes 0 (a / 0 is not
+ * defined).  INT8 rounds half to even; E4M3 as oracle_e4m3_encode. */
+void oracle_quantize_tensor(const void* a, int dtype, int64_t n, float scale, int qtype, uint8_t* q) {
+    for (int64_t i = 0; i < n; ++i) {
+        const float v = load_elem(a, dtype, i);
+        uint8_t code = 0;
+        if (scale != 0.0f) {
+            float t = v / scale;
+            if (qtype == ORACLE_INT8) {
+                t = nearbyintf(t);
+                if (t > 127.0f) t = 127.0f;
+                if (t < -127.0f) t = -127.0f;
+                code = (uint8_t)(int8_t)t;
+            } else {
+                if (t > 448.0f) t = 448.0f;
+                if (t < -448.0f) t = -448.0f;
+                code = oracle_e4m3_encode(t);
+            }
+        }
+        q[i] = code;
+    }
+}
+
+/* Per-tensor weight quantization: s = max|W| / Q over all of W [K, N]; the codes of W / s are
+ * returned transposed, q: [N, K] (row n holds output channel n). */
+int oracle_quant_weight_tensor(const void* w, int dtype, int64_t K, int64_t N, int qtype, uint8_t* q,
+                               float* scale) {
+    uint8_t* t = (uint8_t*)malloc((size_t)(K * N > 0 ? K * N : 1));
+    if (!t) return -1;
+    const float sc = oracle_tensor_scale(oracle_absmax_tensor(w, dtype, K * N), qtype);
+    oracle_quantize_tensor(w, dtype, K * N, sc, qtype, t);
+    for (int64_t j = 0; j < K; ++j)
+        for (int64_t n = 0; n < N; ++n) q[n * K + j] = t[j * N + n];
+    *scale = sc;
+    free(t);
     return 0;
 }

@@ -1,0 +1,177 @@
+"""Pins of the oracle's per-tensor scaling ("Weight-Activation Quantization", s4 "Per-Tensor
+Scaling for FP8", and the per-tensor INT8 example of s2) against things other than itself: the
+page's outlier row, library routines with the same semantics (numpy float32 division and
+round-half-even, torch's float8_e4m3fn cast), closed forms and invariants.
+
+Each test names the kind of mistake it is there to catch.
+"""
+import json
+import os
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def f32(a):
+    return np.asarray(a, dtype=np.float32)
+
+
+def int8_ref(v, scale):
+    """numpy's float32 division, round-half-even and clip: the INT8 recipe of s2 with saturation."""
+    t = (f32(v) / np.float32(scale)).astype(np.float32)
+    return np.clip(np.rint(t), -127, 127).astype(np.int8)
+
+
+def e4m3_ref(v, scale):
+    """torch's E4M3 cast of the fp32 quotient clamped to +-448 (the s4 cast_fp8(x / s))."""
+    with np.errstate(over="ignore"):
+        t = (f32(v) / np.float32(scale)).astype(np.float32)
+    t = np.clip(t, -448, 448)
+    return torch.from_numpy(t).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_absmax_tensor_matches_numpy():
+    """Catches: a maximum over one axis only, a signed instead of absolute maximum, bf16 read as
+    something else."""
+    X = synth.random_matrix((37, 96), seed=3, outliers=2)
+    assert oracle.absmax_tensor(X) == np.max(np.abs(X))
+    Xb = synth.f32_to_bf16_bits(X)
+    assert oracle.absmax_tensor(Xb) == np.max(np.abs(synth.bf16_bits_to_f32(Xb)))
+    neg = -np.abs(X)
+    assert oracle.absmax_tensor(neg) == np.max(np.abs(X))
+    assert oracle.absmax_tensor(np.zeros((3, 16), np.float32)) == 0
+
+
+def test_tensor_scale_closed_form():
+    """s = amax / Q as one fp32 division; catches Q = 128 / 127 mixed up, or amax * Q."""
+    for amax in (80.0, 1.0, 3.7e-3, 448.0 * 2.0 ** -7):
+        assert oracle.tensor_scale(amax, "int8") == np.float32(amax) / np.float32(127)
+        assert oracle.tensor_scale(amax, "fp8") == np.float32(amax) / np.float32(448)
+    assert oracle.tensor_scale(448.0 * 2.0 ** -7, "fp8") == np.float32(2.0 ** -7)
+
+
+def test_outlier_rows_per_tensor():
+    """s2's example as a tensor: the outlier row sets the one scale (80 / 127, printed 0.63) for
+    every row, and every small value of both rows maps to a code of at most 1 (all 0 under
+    round-half-even).  Catches: per-row scales where one tensor scale is meant."""
+    g = golden("outlier_row_per_tensor.json")
+    row = f32(g["row"])
+    small_row = f32([0.3, -0.2, 0.1, 0.25, -0.3, 0.15, 0.05, -0.1])
+    X = np.stack([row, small_row])
+    q, sc = oracle.quant_tensor(X, oracle.absmax_tensor(X), "int8")
+    assert round(float(sc), g["scale_printed_decimals"]) == g["scale_printed"]
+    assert sc == np.float32(80.0) / np.float32(127.0)
+    small = [i for i in range(len(row)) if i not in g["outlier_positions"]]
+    assert np.all(np.abs(q[0, small]) <= g["small_values_max_abs_code"])
+    assert np.all(q[1] == 0)                        # the whole second row is destroyed
+    # per-row scaling keeps the second row (the motivation for per-token scales)
+    q_rows, _ = oracle.quantize_rows(X, "int8")
+    assert np.max(np.abs(q_rows[1])) == 127
+
+
+def test_int8_tensor_matches_numpy():
+    """Catches: multiply by a reciprocal instead of dividing, round-half-away, a missing clamp."""
+    X = synth.random_matrix((48, 160), seed=21, outliers=3)
+    amax = oracle.absmax_tensor(X)
+    q, sc = oracle.quant_tensor(X, amax, "int8")
+    np.testing.assert_array_equal(q, int8_ref(X, sc))
+    assert np.max(np.abs(q)) == 127
+
+
+def test_fp8_tensor_matches_torch():
+    """Catches: a wrong E4M3 flavour (FNUZ, 240), lost signs of zero, a scale off by a factor."""
+    X = synth.random_matrix((40, 128), seed=22, outliers=2)
+    X[0, :4] = [0.0, -0.0, 1e-30, -1e-30]
+    amax = oracle.absmax_tensor(X)
+    q, sc = oracle.quant_tensor(X, amax, "fp8")
+    np.testing.assert_array_equal(q, e4m3_ref(X, sc))
+    dec = np.vectorize(oracle.e4m3_decode)(q)
+    assert np.max(np.abs(dec)) == 448.0
+    # a power-of-two scale: codes are the E4M3 cast of x * 2^-k itself
+    X2 = X / np.float32(amax) * np.float32(448.0 * 2.0 ** -5)
+    q2, sc2 = oracle.quant_tensor(X2, oracle.absmax_tensor(X2), "fp8")
+    assert sc2 == np.float32(2.0 ** -5)
+    ref = torch.from_numpy((X2 * np.float32(32.0)).astype(np.float32)).to(torch.float8_e4m3fn)
+    np.testing.assert_array_equal(q2, ref.view(torch.uint8).numpy())
+
+
+def test_dequantized_tensor_within_half_spacing():
+    """x^ = s q (s4): every value decodes to within half an E4M3 spacing of x / s (relative 2^-4
+    for normal codes, 2^-10 absolute in the subnormal range).  Catches: truncation instead of
+    rounding, a scale applied twice."""
+    X = synth.random_matrix((32, 128), seed=23, outliers=2)
+    q, sc = oracle.quant_tensor(X, oracle.absmax_tensor(X), "fp8")
+    dec = np.vectorize(oracle.e4m3_decode)(q).astype(np.float64)
+    t = X.astype(np.float64) / float(sc)
+    bound = np.maximum(np.abs(t) * 2.0 ** -4, 2.0 ** -10)
+    assert np.all(np.abs(dec - t) <= bound * (1 + 1e-12))
+
+
+def test_delayed_scaling_saturates():
+    """Delayed scaling (s4 table): the scale comes from an earlier, smaller maximum, so values
+    beyond Q s clamp to the top code and the rest round as usual.  Catches: wrap-around instead of
+    saturation, the scale recomputed from the current tensor."""
+    X = synth.random_matrix((24, 128), seed=24, outliers=2)
+    amax = oracle.absmax_tensor(X)
+    prev = np.float32(amax / 4)
+    for qt, top in (("int8", 127), ("fp8", 448.0)):
+        q, sc = oracle.quant_tensor(X, prev, qt)
+        assert sc == oracle.tensor_scale(prev, qt)
+        ref = int8_ref(X, sc) if qt == "int8" else e4m3_ref(X, sc)
+        np.testing.assert_array_equal(q, ref)
+        mag = np.abs(q.astype(np.float64)) if qt == "int8" else np.abs(np.vectorize(oracle.e4m3_decode)(q))
+        over = np.abs(X.astype(np.float64)) / float(sc) > top
+        assert over.any() and np.all(mag[over] == top)
+
+
+def test_zero_tensor_and_zero_history():
+    """A zero maximum gives scale 0 and all-zero codes (x / 0 is not defined), as for rows."""
+    X = synth.random_matrix((4, 32), seed=25)
+    for qt in ("int8", "fp8"):
+        q, sc = oracle.quant_tensor(X, 0.0, qt)
+        assert sc == 0 and np.all(q == 0)
+
+
+def test_weight_tensor_orientation_and_scale():
+    """W [K, N] -> codes [N, K] with one scale max|W| / Q.  Catches: codes not transposed, a
+    per-column scale where one tensor scale is meant."""
+    W = synth.random_matrix((64, 24), seed=26, scale=0.02)
+    W[5, 7] = 0.5                                   # one large weight sets the tensor scale
+    for qt in ("int8", "fp8"):
+        q, sc = oracle.quant_weight_tensor(W, qt)
+        assert q.shape == (24, 64)
+        assert sc == oracle.tensor_scale(np.float32(0.5), qt)
+        ref = int8_ref(W, sc) if qt == "int8" else e4m3_ref(W, sc)
+        np.testing.assert_array_equal(q, ref.T)
+
+
+def test_layer_tensor_int8_worse_than_smoothquant_on_outliers():
+    """The pages' point (s2, s3): on activations with outlier channels, one INT8 scale per tensor
+    loses more than per-token scales with smoothing.  Direction only, on the tiny workload."""
+    X, W = synth.make_inputs("c1")
+    ref = X.astype(np.float64) @ W.astype(np.float64)
+    e_t = np.linalg.norm(oracle.layer_tensor(X, W, "int8")["y64"] - ref) / np.linalg.norm(ref)
+    e_s = np.linalg.norm(oracle.layer(X, W, 0.5, "int8")["y64"] - ref) / np.linalg.norm(ref)
+    assert e_s < e_t
+
+
+def test_layer_tensor_fp8_dequant_closed_form():
+    """Per-tensor FP8 through the GEMM: y64 = (exact sum of decoded products) s_x s_w.  Checked by
+    brute force on a small case.  Catches: a scale left out, the wrong operand transposed."""
+    X = synth.random_matrix((6, 32), seed=27, outliers=1)
+    W = synth.random_matrix((32, 5), seed=28, scale=0.05)
+    out = oracle.layer_tensor(X, W, "fp8")
+    dx = np.vectorize(oracle.e4m3_decode)(out["qx"]).astype(np.float64)
+    dw = np.vectorize(oracle.e4m3_decode)(out["qw"]).astype(np.float64)
+    brute = (dx @ dw.T) * float(out["sx"]) * float(out["sw"])
+    np.testing.assert_allclose(out["y64"], brute, rtol=1e-15, atol=0)
