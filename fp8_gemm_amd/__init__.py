@@ -25,7 +25,8 @@ W8A8_F32, W8A8_BF16 = 0, 1
 W8A8_INT8, W8A8_FP8_E4M3 = 0, 1
 
 ENTRY_POINTS = ("w8a8_smooth_scales", "w8a8_fold_quant_weight", "w8a8_quant_act", "w8a8_gemm_dequant",
-                "w8a8_gemm_i32", "w8a8_gemm_f32", "w8a8_status_string", "w8a8_version")
+                "w8a8_gemm_i32", "w8a8_gemm_f32", "w8a8_absmax", "w8a8_quant_act_tensor",
+                "w8a8_quant_weight_tensor", "w8a8_gemm_dequant_tensor", "w8a8_status_string", "w8a8_version")
 
 
 class W8A8Error(RuntimeError):
@@ -52,6 +53,10 @@ def _load() -> ctypes.CDLL:
         "w8a8_gemm_dequant": (I, [P, P, P, P, I, I64, I64, I64, P, P]),
         "w8a8_gemm_i32": (I, [P, P, I64, I64, I64, P, P]),
         "w8a8_gemm_f32": (I, [P, P, I64, I64, I64, P, P]),
+        "w8a8_absmax": (I, [P, I, I64, P, I, P]),
+        "w8a8_quant_act_tensor": (I, [P, I, I64, I64, P, I, P, P, P, I, P]),
+        "w8a8_quant_weight_tensor": (I, [P, I, I64, I64, I, P, P, P]),
+        "w8a8_gemm_dequant_tensor": (I, [P, P, P, P, I, I64, I64, I64, P, P]),
         "w8a8_status_string": (ctypes.c_char_p, [I]),
         "w8a8_version": (ctypes.c_char_p, []),
     }
@@ -207,3 +212,73 @@ def w8a8_layer(x, w, alpha: float = 0.5, qtype="int8", stream=None):
     xq, x_scale = w8a8_quant_act(x, s, qtype, stream=stream)
     y = w8a8_gemm_dequant(xq, x_scale, wq, w_scale, qtype, stream=stream)
     return dict(ax=ax, aw=aw, s=s, wq=wq, w_scale=w_scale, xq=xq, x_scale=x_scale, y=y)
+
+
+# ---- per-tensor scaling (one scale per tensor, held in a 1-element float32 tensor) ----------------
+
+def w8a8_absmax(a, amax=None, accumulate: bool = False, stream=None):
+    """max |a| over the whole tensor, into a float32 [1] tensor (merged with it if accumulate)."""
+    _dev(a, "a")
+    amax = torch.empty(1, dtype=torch.float32, device=a.device) if amax is None else _dev(amax, "amax")
+    _check("w8a8_absmax", _load().w8a8_absmax(_ptr(a), _dtype(a), a.numel(), _ptr(amax), int(bool(accumulate)),
+                                              _stream(stream)))
+    return amax
+
+
+def w8a8_quant_act_tensor(x, amax_in, qtype="fp8", xq=None, x_scale=None, amax_out=None, track: bool = False,
+                          accumulate: bool = False, stream=None):
+    """X [M, K] -> (codes [M, K], the one scale float32 [1], amax_out or None) with the scale
+    amax_in / Q.  track: also return this X's maximum (for the next step's amax_in)."""
+    _dev(x, "x"), _dev(amax_in, "amax_in")
+    q = _qtype(qtype)
+    M, K = x.shape
+    xq = torch.empty((M, K), dtype=_code_dtype(q), device=x.device) if xq is None else _dev(xq, "xq")
+    x_scale = torch.empty(1, dtype=torch.float32, device=x.device) if x_scale is None else _dev(x_scale, "x_scale")
+    if track and amax_out is None:
+        amax_out = torch.empty(1, dtype=torch.float32, device=x.device)
+    _dev(amax_out, "amax_out")
+    _check("w8a8_quant_act_tensor", _load().w8a8_quant_act_tensor(
+        _ptr(x), _dtype(x), M, K, _ptr(amax_in), q, _ptr(xq), _ptr(x_scale), _ptr(amax_out),
+        int(bool(accumulate)), _stream(stream)))
+    return xq, x_scale, amax_out
+
+
+def w8a8_quant_weight_tensor(w, qtype="fp8", wq=None, w_scale=None, stream=None):
+    """W [K, N] -> (codes [N, K], the one scale float32 [1] = max|W| / Q)."""
+    _dev(w, "w")
+    q = _qtype(qtype)
+    K, N = w.shape
+    wq = torch.empty((N, K), dtype=_code_dtype(q), device=w.device) if wq is None else _dev(wq, "wq")
+    w_scale = torch.empty(1, dtype=torch.float32, device=w.device) if w_scale is None else _dev(w_scale, "w_scale")
+    _check("w8a8_quant_weight_tensor", _load().w8a8_quant_weight_tensor(
+        _ptr(w), _dtype(w), K, N, q, _ptr(wq), _ptr(w_scale), _stream(stream)))
+    return wq, w_scale
+
+
+def w8a8_gemm_dequant_tensor(xq, x_scale, wq, w_scale, qtype="fp8", y=None, stream=None):
+    """Quantized GEMM + dequantize with one scale per operand: Y bfloat16 [M, N]."""
+    for t, n in ((xq, "xq"), (x_scale, "x_scale"), (wq, "wq"), (w_scale, "w_scale")):
+        _dev(t, n)
+    q = _qtype(qtype)
+    M, K = xq.shape
+    N, K2 = wq.shape
+    if K2 != K:
+        raise ValueError("xq is [M, K] and wq is [N, K]")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device) if y is None else _dev(y, "y")
+    _check("w8a8_gemm_dequant_tensor", _load().w8a8_gemm_dequant_tensor(
+        _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), q, M, N, K, _ptr(y), _stream(stream)))
+    return y
+
+
+def w8a8_layer_tensor(x, w, qtype="fp8", amax_prev=None, stream=None):
+    """The per-tensor path: one scale for W (its own maximum) and one for X, from this X's maximum
+    (amax_prev None: current scaling, two passes over X) or an earlier step's (delayed scaling: one
+    pass that also returns this X's maximum as amax for the next step)."""
+    wq, w_scale = w8a8_quant_weight_tensor(w, qtype, stream=stream)
+    if amax_prev is None:
+        amax = w8a8_absmax(x, stream=stream)
+        xq, x_scale, _ = w8a8_quant_act_tensor(x, amax, qtype, stream=stream)
+    else:
+        xq, x_scale, amax = w8a8_quant_act_tensor(x, amax_prev, qtype, track=True, stream=stream)
+    y = w8a8_gemm_dequant_tensor(xq, x_scale, wq, w_scale, qtype, stream=stream)
+    return dict(wq=wq, w_scale=w_scale, xq=xq, x_scale=x_scale, amax=amax, y=y)

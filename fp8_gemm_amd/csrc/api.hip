@@ -14,6 +14,7 @@ constexpr int64_t kMaxDim = int64_t(1) << 31;   // per-dimension limit (32-bit g
 constexpr int64_t kMaxKInt8 = 133144;           // K * 127^2 < 2^31
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 bool valid_dtype(w8a8_dtype t) { return t == W8A8_F32 || t == W8A8_BF16; }
 bool valid_qtype(w8a8_qtype t) { return t == W8A8_INT8 || t == W8A8_FP8_E4M3; }
@@ -69,7 +70,7 @@ W8A8_API w8a8_status w8a8_fold_quant_weight(const void* w, w8a8_dtype w_dtype, i
     hipError_t e = w8a8::launch_fill(w_scale, N, 0.0f, stream);
     if (e == hipSuccess) e = w8a8::launch_absmax_cols(w, bf16, K, N, s, fp8 ? 448.0f : 127.0f, w_scale, stream);
     if (e == hipSuccess)
-        e = w8a8::launch_quant_weight_t(w, bf16, K, N, s, w_scale, fp8, static_cast<uint8_t*>(wq), stream);
+        e = w8a8::launch_quant_weight_t(w, bf16, K, N, s, w_scale, false, fp8, static_cast<uint8_t*>(wq), stream);
     return from_hip(e);
 }
 
@@ -97,8 +98,8 @@ W8A8_API w8a8_status w8a8_gemm_dequant(const void* xq, const float* x_scale, con
     if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned16(x_scale) || !aligned16(w_scale))
         return W8A8_ERR_UNSUPPORTED;
     return from_hip(w8a8::launch_gemm(static_cast<const uint8_t*>(xq), x_scale, static_cast<const uint8_t*>(wq),
-                                      w_scale, qtype == W8A8_FP8_E4M3, M, N, K, static_cast<uint16_t*>(y), nullptr,
-                                      stream));
+                                      w_scale, qtype == W8A8_FP8_E4M3, false, M, N, K, static_cast<uint16_t*>(y),
+                                      nullptr, stream));
 }
 
 W8A8_API w8a8_status w8a8_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t M, int64_t N, int64_t K,
@@ -110,8 +111,8 @@ W8A8_API w8a8_status w8a8_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t M
     if (M == 0 || N == 0) return W8A8_OK;
     if (!aligned16(xq) || !aligned16(wq) || !aligned16(acc)) return W8A8_ERR_UNSUPPORTED;
     return from_hip(w8a8::launch_gemm(reinterpret_cast<const uint8_t*>(xq), nullptr,
-                                      reinterpret_cast<const uint8_t*>(wq), nullptr, false, M, N, K, nullptr, acc,
-                                      stream));
+                                      reinterpret_cast<const uint8_t*>(wq), nullptr, false, false, M, N, K, nullptr,
+                                      acc, stream));
 }
 
 W8A8_API w8a8_status w8a8_gemm_f32(const uint8_t* xq, const uint8_t* wq, int64_t M, int64_t N, int64_t K,
@@ -121,7 +122,71 @@ W8A8_API w8a8_status w8a8_gemm_f32(const uint8_t* xq, const uint8_t* wq, int64_t
     if (st != W8A8_OK) return st;
     if (M == 0 || N == 0) return W8A8_OK;
     if (!aligned16(xq) || !aligned16(wq) || !aligned16(acc)) return W8A8_ERR_UNSUPPORTED;
-    return from_hip(w8a8::launch_gemm(xq, nullptr, wq, nullptr, true, M, N, K, nullptr, acc, stream));
+    return from_hip(w8a8::launch_gemm(xq, nullptr, wq, nullptr, true, false, M, N, K, nullptr, acc, stream));
+}
+
+// ---- per-tensor scaling -------------------------------------------------------------------------
+
+W8A8_API w8a8_status w8a8_absmax(const void* a, w8a8_dtype dtype, int64_t n, float* amax, int accumulate,
+                                 hipStream_t stream) {
+    if (!amax || !valid_dtype(dtype) || n < 0) return W8A8_ERR_INVALID_ARG;
+    if (n > 0 && !a) return W8A8_ERR_INVALID_ARG;
+    if (n % 8 != 0 || !aligned16(a) || !aligned4(amax)) return W8A8_ERR_UNSUPPORTED;
+    hipError_t e = hipSuccess;
+    if (!accumulate) e = w8a8::launch_fill(amax, 1, 0.0f, stream);
+    if (e == hipSuccess) e = w8a8::launch_absmax_tensor(a, dtype == W8A8_BF16, n, 0.0f, amax, stream);
+    return from_hip(e);
+}
+
+W8A8_API w8a8_status w8a8_quant_act_tensor(const void* x, w8a8_dtype x_dtype, int64_t M, int64_t K,
+                                           const float* amax_in, w8a8_qtype qtype, void* xq, float* x_scale,
+                                           float* amax_out, int accumulate, hipStream_t stream) {
+    if (!valid_dtype(x_dtype) || !valid_qtype(qtype) || !amax_in || !x_scale) return W8A8_ERR_INVALID_ARG;
+    if (M > 0 && (!x || !xq)) return W8A8_ERR_INVALID_ARG;
+    if (amax_out && amax_out == amax_in) return W8A8_ERR_INVALID_ARG;
+    w8a8_status st = check_dims(M, 0, K);
+    if (st != W8A8_OK) return st;
+    if (!aligned16(x) || !aligned16(xq) || !aligned4(amax_in) || !aligned4(x_scale) || !aligned4(amax_out))
+        return W8A8_ERR_UNSUPPORTED;
+    hipError_t e = hipSuccess;
+    if (amax_out && !accumulate) e = w8a8::launch_fill(amax_out, 1, 0.0f, stream);
+    if (e == hipSuccess)     // M == 0 still writes x_scale
+        e = w8a8::launch_quant_tensor(x, x_dtype == W8A8_BF16, M * K, amax_in, qtype == W8A8_FP8_E4M3,
+                                      static_cast<uint8_t*>(xq), x_scale, amax_out, stream);
+    return from_hip(e);
+}
+
+W8A8_API w8a8_status w8a8_quant_weight_tensor(const void* w, w8a8_dtype w_dtype, int64_t K, int64_t N,
+                                              w8a8_qtype qtype, void* wq, float* w_scale, hipStream_t stream) {
+    if (!valid_dtype(w_dtype) || !valid_qtype(qtype) || !w_scale) return W8A8_ERR_INVALID_ARG;
+    if (N > 0 && (!w || !wq)) return W8A8_ERR_INVALID_ARG;
+    w8a8_status st = check_dims(0, N, K);
+    if (st != W8A8_OK) return st;
+    if (!aligned16(w) || !aligned16(wq) || !aligned4(w_scale)) return W8A8_ERR_UNSUPPORTED;
+    const bool bf16 = w_dtype == W8A8_BF16, fp8 = qtype == W8A8_FP8_E4M3;
+    // The maximum divided by Q, merged block by block (correctly rounded division is monotone, so
+    // the merged value is max|W| / Q rounded once); then the codes with that one scale.
+    hipError_t e = w8a8::launch_fill(w_scale, 1, 0.0f, stream);
+    if (e == hipSuccess && N > 0) e = w8a8::launch_absmax_tensor(w, bf16, K * N, fp8 ? 448.0f : 127.0f, w_scale, stream);
+    if (e == hipSuccess && N > 0)
+        e = w8a8::launch_quant_weight_t(w, bf16, K, N, nullptr, w_scale, true, fp8, static_cast<uint8_t*>(wq), stream);
+    return from_hip(e);
+}
+
+W8A8_API w8a8_status w8a8_gemm_dequant_tensor(const void* xq, const float* x_scale, const void* wq,
+                                              const float* w_scale, w8a8_qtype qtype, int64_t M, int64_t N,
+                                              int64_t K, void* y, hipStream_t stream) {
+    if (!valid_qtype(qtype)) return W8A8_ERR_INVALID_ARG;
+    if (M > 0 && N > 0 && (!xq || !x_scale || !wq || !w_scale || !y)) return W8A8_ERR_INVALID_ARG;
+    w8a8_status st = check_dims(M, N, K);
+    if (st != W8A8_OK) return st;
+    if (qtype == W8A8_INT8 && K > kMaxKInt8) return W8A8_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return W8A8_OK;
+    if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || !aligned4(x_scale) || !aligned4(w_scale))
+        return W8A8_ERR_UNSUPPORTED;
+    return from_hip(w8a8::launch_gemm(static_cast<const uint8_t*>(xq), x_scale, static_cast<const uint8_t*>(wq),
+                                      w_scale, qtype == W8A8_FP8_E4M3, true, M, N, K, static_cast<uint16_t*>(y),
+                                      nullptr, stream));
 }
 
 W8A8_API const char* w8a8_status_string(w8a8_status status) {

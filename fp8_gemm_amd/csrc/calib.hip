@@ -4,6 +4,8 @@
 // Both reductions are HBM-bound streams.  Loads are 16 bytes per lane (8 bf16 or 2x4 fp32), a
 // wave covers 512 consecutive columns of a row, and every maximum is exact (fp32 max needs no
 // rounding), so the result does not depend on how the work is split.
+#include <algorithm>
+
 #include "device.h"
 #include "launch.h"
 
@@ -137,6 +139,41 @@ __global__ void smooth_factors_kernel(const float* __restrict__ ax, const float*
     s[j] = smooth_factor(ax[j], aw[j], alpha);
 }
 
+// Maximum of |a| over a whole tensor of nchunk 16-byte chunks (8 elements each), divided by
+// divisor when it is not 0.  Each thread keeps 8 chunks in flight per step of a grid-stride loop
+// (chunks past the end re-read the last one); the block's maximum is merged into out[0] with an
+// atomic maximum, skipped when out[0] already holds at least as much (out[0] only grows, so a
+// stale read can only cause a redundant atomic, never a missed one).
+template <bool kBf16>
+__global__ __launch_bounds__(256) void absmax_tensor_kernel(const void* __restrict__ a, int64_t nchunk, float divisor,
+                                                            float* __restrict__ out) {
+    __shared__ float part[4];
+    constexpr int kU = 8;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    float m = 0.0f;
+    for (int64_t c0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c0 < nchunk; c0 += kU * stride) {
+        float v[kU][8];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t c = c0 + u * stride;
+            load8<kBf16>(a, (c < nchunk ? c : nchunk - 1) * 8, v[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[u][e]));
+    }
+    m = wave_max(m);
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    if (lane == 0) part[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float b = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+        if (divisor != 0.0f) b = div_rn(b, divisor);
+        if (b > *out) atomic_max_nonneg(out, b);
+    }
+}
+
 template <bool kBf16, bool kVec>
 void cols_launch(dim3 grid, const void* a, int64_t R, int64_t C, const float* row_scale, float divisor, float* out,
                  hipStream_t st) {
@@ -184,6 +221,19 @@ hipError_t launch_absmax_rows(const void* a, bool bf16, int64_t R, int64_t C, fl
         if (vec) hipLaunchKernelGGL((absmax_rows_kernel<false, true>), grid, dim3(256), 0, st, a, R, C, out, ax, alpha, s);
         else hipLaunchKernelGGL((absmax_rows_kernel<false, false>), grid, dim3(256), 0, st, a, R, C, out, ax, alpha, s);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_absmax_tensor(const void* a, bool bf16, int64_t n, float divisor, float* out, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    const int64_t nchunk = n / 8;
+    const int64_t blocks = std::min<int64_t>((nchunk + 256 * 8 - 1) / (256 * 8), 4096);
+    if (bf16)
+        hipLaunchKernelGGL(absmax_tensor_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a, nchunk,
+                           divisor, out);
+    else
+        hipLaunchKernelGGL(absmax_tensor_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a, nchunk,
+                           divisor, out);
     return hipGetLastError();
 }
 

@@ -86,10 +86,10 @@ __device__ __forceinline__ int out_col(int lane, int g) {
 }
 
 // Dequantize and store four consecutive outputs of row m starting at column n (or store the raw
-// accumulators when kOutAcc).
+// accumulators when kOutAcc).  tensor: one scale for all of W (w_scale[0]) instead of one per column.
 template <bool kOutAcc, typename T>
 __device__ __forceinline__ void store4(const T (&a)[4], int64_t m, int64_t n, int64_t M, int64_t N, float sxm,
-                                       const float* __restrict__ w_scale, uint16_t* __restrict__ y,
+                                       const float* __restrict__ w_scale, bool tensor, uint16_t* __restrict__ y,
                                        void* __restrict__ out_acc) {
     if (m >= M) return;
     if constexpr (kOutAcc) {
@@ -106,7 +106,7 @@ __device__ __forceinline__ void store4(const T (&a)[4], int64_t m, int64_t n, in
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float swn = (n + r < N) ? w_scale[n + r] : 0.0f;
+            const float swn = (n + r < N) ? w_scale[tensor ? 0 : n + r] : 0.0f;
             v[r] = (static_cast<float>(a[r]) * sxm) * swn;
         }
         const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
@@ -124,18 +124,19 @@ __device__ __forceinline__ void store4(const T (&a)[4], int64_t m, int64_t n, in
 }
 
 // Epilogue of one kTile x kTile accumulator block whose rows start at m_base and columns at n_base.
+// tensor: x_scale[0] and w_scale[0] are the one scale of each operand (per-tensor scaling).
 template <typename MM, bool kOutAcc>
 __device__ __forceinline__ void store_block(const typename MM::Acc& acc, int64_t m_base, int64_t n_base, int lane,
                                             int64_t M, int64_t N, const float* __restrict__ x_scale,
-                                            const float* __restrict__ w_scale, uint16_t* __restrict__ y,
-                                            void* __restrict__ out_acc) {
+                                            const float* __restrict__ w_scale, bool tensor,
+                                            uint16_t* __restrict__ y, void* __restrict__ out_acc) {
     using T = typename std::remove_cv<typename std::remove_reference<decltype(acc[0])>::type>::type;
     const int64_t m = m_base + out_row<MM::kTile>(lane);
-    const float sxm = (!kOutAcc && m < M) ? x_scale[m] : 0.0f;
+    const float sxm = (!kOutAcc && m < M) ? x_scale[tensor ? 0 : m] : 0.0f;
 #pragma unroll
     for (int g = 0; g < MM::kGroups; ++g) {
         const T a[4] = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
-        store4<kOutAcc>(a, m, n_base + out_col<MM::kTile>(lane, g), M, N, sxm, w_scale, y, out_acc);
+        store4<kOutAcc>(a, m, n_base + out_col<MM::kTile>(lane, g), M, N, sxm, w_scale, tensor, y, out_acc);
     }
 }
 
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(kGM * kGN * kWave, 1)
 __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void gemm_tile_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ x_scale, const uint8_t* __restrict__ wq,
     const float* __restrict__ w_scale, int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y,
-    void* __restrict__ out_acc, int tiles_m, int tiles_n, int group_m) {
+    void* __restrict__ out_acc, int tiles_m, int tiles_n, int group_m, int tensor_scales) {
     using Acc = typename MM::Acc;
     constexpr int kWaves = kGM * kGN;                 // a kGM x kGN grid of waves
     constexpr int kWM = kBM / kGM, kWN = kBN / kGN;   // each wave's kWM x kWN outputs
@@ -313,14 +314,17 @@ __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void gemm_til
 #pragma unroll
         for (int i = 0; i < kMT; ++i) {
             const int64_t m = mw0 + i * MM::kTile + out_row<MM::kTile>(lane);
-            sx_l[i] = m < M ? x_scale[m] : 0.0f;
+            sx_l[i] = m < M ? x_scale[tensor_scales ? 0 : m] : 0.0f;
         }
 #pragma unroll
         for (int j = 0; j < kNT; ++j)
 #pragma unroll
             for (int g = 0; g < kG; ++g) {
                 const int64_t n = nw0 + j * MM::kTile + out_col<MM::kTile>(lane, g);
-                if (n + 3 < N) {
+                if (tensor_scales) {
+                    const float w0 = w_scale[0];
+                    sw_l[j][g] = v4f{w0, w0, w0, w0};
+                } else if (n + 3 < N) {
                     sw_l[j][g] = *reinterpret_cast<const v4f*>(w_scale + n);
                 } else {
 #pragma unroll
@@ -517,7 +521,7 @@ __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void gemm_til
 #pragma unroll
             for (int j = 0; j < kNT; ++j)
                 store_block<MM, kOutAcc>(acc[i][j], mw0 + i * MM::kTile, nw0 + j * MM::kTile, lane, M, N, x_scale,
-                                         w_scale, y, out_acc);
+                                         w_scale, tensor_scales != 0, y, out_acc);
     } else {
         // Dequantize in registers, stage the wave's kWM x kWN bf16 tile in LDS (rows padded to
         // kOutStride bytes), and write it back as 16-byte pieces of whole output rows.
@@ -571,7 +575,7 @@ template <int kMT, typename MM, bool kOutAcc>
 __global__ __launch_bounds__(kThreads) void gemm_small_m_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ x_scale, const uint8_t* __restrict__ wq,
     const float* __restrict__ w_scale, int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y,
-    void* __restrict__ out_acc) {
+    void* __restrict__ out_acc, int tensor_scales) {
     using Acc = typename MM::Acc;
     static_assert(MM::kTile == 16, "16x16 blocks");
     __shared__ Acc red[3][kMT][kWave];
@@ -642,7 +646,8 @@ __global__ __launch_bounds__(kThreads) void gemm_small_m_kernel(
             Acc a = acc[i];
 #pragma unroll
             for (int w = 0; w < 3; ++w) a += red[w][i][lane];
-            store_block<MM, kOutAcc>(a, static_cast<int64_t>(i) * 16, n0, lane, M, N, x_scale, w_scale, y, out_acc);
+            store_block<MM, kOutAcc>(a, static_cast<int64_t>(i) * 16, n0, lane, M, N, x_scale, w_scale,
+                                     tensor_scales != 0, y, out_acc);
         }
     }
 }
@@ -659,7 +664,7 @@ template <int kS, typename MM, bool kOutAcc>
 __global__ __launch_bounds__(kThreads) void gemm_decode_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ x_scale, const uint8_t* __restrict__ wq,
     const float* __restrict__ w_scale, int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y,
-    void* __restrict__ out_acc) {
+    void* __restrict__ out_acc, int tensor_scales) {
     using Acc = typename MM::Acc;
     static_assert(MM::kTile == 16, "16x16 blocks");
     constexpr int kC = MM::kChunks;
@@ -703,7 +708,8 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_kernel(
             Acc a = acc;
 #pragma unroll
             for (int w = 0; w < 3; ++w) a += red[w][lane];
-            store_block<MM, kOutAcc>(a, 0, static_cast<int64_t>(t) * 16, lane, M, N, x_scale, w_scale, y, out_acc);
+            store_block<MM, kOutAcc>(a, 0, static_cast<int64_t>(t) * 16, lane, M, N, x_scale, w_scale,
+                                     tensor_scales != 0, y, out_acc);
         }
         __syncthreads();                 // red is reused by the next tile
     };
@@ -717,27 +723,27 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_kernel(
 
 template <typename M16, typename MT, bool kOutAcc>
 hipError_t gemm_dispatch(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale,
-                         int64_t M, int64_t N, int64_t K, uint16_t* y, void* out_acc, hipStream_t st) {
+                         int64_t M, int64_t N, int64_t K, uint16_t* y, void* out_acc, int tensor, hipStream_t st) {
     if (M <= 16 && K == 4 * 16 * M16::kKStep) {
         // decode shape: X in registers, persistent grid with an equal number of tiles per block
         const int64_t ntiles = (N + 15) / 16;
         const int64_t per_block = (ntiles + 511) / 512;
         const int64_t grid = (ntiles + per_block - 1) / per_block;
         hipLaunchKernelGGL((gemm_decode_kernel<16, M16, kOutAcc>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
-                           st, xq, x_scale, wq, w_scale, M, N, K, y, out_acc);
+                           st, xq, x_scale, wq, w_scale, M, N, K, y, out_acc, tensor);
         return hipGetLastError();
     }
     if (M <= 64) {
         dim3 grid(static_cast<unsigned>((N + 15) / 16));
         if (M <= 16)
             hipLaunchKernelGGL((gemm_small_m_kernel<1, M16, kOutAcc>), grid, dim3(kThreads), 0, st, xq, x_scale, wq,
-                               w_scale, M, N, K, y, out_acc);
+                               w_scale, M, N, K, y, out_acc, tensor);
         else if (M <= 32)
             hipLaunchKernelGGL((gemm_small_m_kernel<2, M16, kOutAcc>), grid, dim3(kThreads), 0, st, xq, x_scale, wq,
-                               w_scale, M, N, K, y, out_acc);
+                               w_scale, M, N, K, y, out_acc, tensor);
         else
             hipLaunchKernelGGL((gemm_small_m_kernel<4, M16, kOutAcc>), grid, dim3(kThreads), 0, st, xq, x_scale, wq,
-                               w_scale, M, N, K, y, out_acc);
+                               w_scale, M, N, K, y, out_acc, tensor);
         return hipGetLastError();
     }
     const int group_m = 4;
@@ -750,14 +756,14 @@ hipError_t gemm_dispatch(const uint8_t* xq, const float* x_scale, const uint8_t*
         const int tiles_n = static_cast<int>((N + kBN - 1) / kBN);
         hipLaunchKernelGGL((gemm_tile_kernel<kBM, kBN, kGM, kGN, 2, 1, MT, kOutAcc>), dim3(tiles_m * tiles_n),
                            dim3(kGM * kGN * kWave), 0, st, xq, x_scale, wq, w_scale, M, N, K, y, out_acc, tiles_m,
-                           tiles_n, group_m);
+                           tiles_n, group_m, tensor);
     } else {
         constexpr int kBM = 256, kBN = 128, kGM = 4, kGN = 2;
         const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
         const int tiles_n = static_cast<int>((N + kBN - 1) / kBN);
         hipLaunchKernelGGL((gemm_tile_kernel<kBM, kBN, kGM, kGN, 3, 2, MT, kOutAcc>), dim3(tiles_m * tiles_n),
                            dim3(kGM * kGN * kWave), 0, st, xq, x_scale, wq, w_scale, M, N, K, y, out_acc, tiles_m,
-                           tiles_n, group_m);
+                           tiles_n, group_m, tensor);
     }
     return hipGetLastError();
 }
@@ -765,14 +771,16 @@ hipError_t gemm_dispatch(const uint8_t* xq, const float* x_scale, const uint8_t*
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, bool fp8,
-                       int64_t M, int64_t N, int64_t K, uint16_t* y, void* out_acc, hipStream_t st) {
+                       bool tensor_scales, int64_t M, int64_t N, int64_t K, uint16_t* y, void* out_acc,
+                       hipStream_t st) {
     if (M <= 0 || N <= 0) return hipSuccess;
     if (out_acc) {
-        if (fp8) return gemm_dispatch<MmaF8x16, MmaF8x32, true>(xq, nullptr, wq, nullptr, M, N, K, nullptr, out_acc, st);
-        return gemm_dispatch<MmaI8x16, MmaI8x32, true>(xq, nullptr, wq, nullptr, M, N, K, nullptr, out_acc, st);
+        if (fp8) return gemm_dispatch<MmaF8x16, MmaF8x32, true>(xq, nullptr, wq, nullptr, M, N, K, nullptr, out_acc, 0, st);
+        return gemm_dispatch<MmaI8x16, MmaI8x32, true>(xq, nullptr, wq, nullptr, M, N, K, nullptr, out_acc, 0, st);
     }
-    if (fp8) return gemm_dispatch<MmaF8x16, MmaF8x32, false>(xq, x_scale, wq, w_scale, M, N, K, y, nullptr, st);
-    return gemm_dispatch<MmaI8x16, MmaI8x32, false>(xq, x_scale, wq, w_scale, M, N, K, y, nullptr, st);
+    const int t = tensor_scales ? 1 : 0;
+    if (fp8) return gemm_dispatch<MmaF8x16, MmaF8x32, false>(xq, x_scale, wq, w_scale, M, N, K, y, nullptr, t, st);
+    return gemm_dispatch<MmaI8x16, MmaI8x32, false>(xq, x_scale, wq, w_scale, M, N, K, y, nullptr, t, st);
 }
 
 }  // namespace w8a8

@@ -30,15 +30,27 @@ hipError_t launch_quant_act(const void* x, bool bf16, int64_t M, int64_t K, cons
                             uint8_t* xq, float* x_scale, hipStream_t st);
 
 // Quantize W~ = s * W [K, N] with the per-column scales w_scale [N] (from launch_absmax_cols with
-// divisor 127 or 448) and write the codes transposed, wq [N, K].
+// divisor 127 or 448), or with tensor_scale the one scale w_scale[0], and write the codes
+// transposed, wq [N, K].
 hipError_t launch_quant_weight_t(const void* w, bool bf16, int64_t K, int64_t N, const float* s,
-                                 const float* w_scale, bool fp8, uint8_t* wq, hipStream_t st);
+                                 const float* w_scale, bool tensor_scale, bool fp8, uint8_t* wq, hipStream_t st);
+
+// out[0] = max(out[0], max_i |a[i]| / divisor (rounded once; divisor 0: no division)) over n
+// elements, n a multiple of 8, a 16-byte aligned.  Exact; blocks merge with an atomic maximum.
+hipError_t launch_absmax_tensor(const void* a, bool bf16, int64_t n, float divisor, float* out, hipStream_t st);
+
+// Per-tensor quantize of n elements (a multiple of 8): scale = amax_in[0] / Q, q[i] = code of
+// a[i] / scale saturated at +-Q (scale 0: codes 0), scale_out[0] = scale.  amax_out != nullptr:
+// max_i |a[i]| is merged into amax_out[0] in the same pass (it must not be amax_in).
+hipError_t launch_quant_tensor(const void* a, bool bf16, int64_t n, const float* amax_in, bool fp8, uint8_t* q,
+                               float* scale_out, float* amax_out, hipStream_t st);
 
 // GEMM over K-contiguous operands xq [M, K] and wq [N, K]:
 //   acc != nullptr: the raw accumulators [M, N] (int32 for INT8, fp32 for E4M3)
-//   else: y bf16 [M, N] = ((float)acc * x_scale[m]) * w_scale[n].
+//   else: y bf16 [M, N] = ((float)acc * x_scale[m]) * w_scale[n], or with tensor_scales the one
+//   scale of each operand, x_scale[0] and w_scale[0].
 hipError_t launch_gemm(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale,
-                       bool fp8, int64_t M, int64_t N, int64_t K, uint16_t* y, void* acc,
+                       bool fp8, bool tensor_scales, int64_t M, int64_t N, int64_t K, uint16_t* y, void* acc,
                        hipStream_t st);
 
 }  // namespace w8a8

@@ -304,7 +304,7 @@ __device__ __forceinline__ void code_item(const WeightItem<kBf16, kVec>& it, con
 template <bool kBf16, bool kFp8, bool kVec>
 __global__ __launch_bounds__(256) void quant_weight_t_kernel(const void* __restrict__ w, int64_t K, int64_t N,
                                                              const float* __restrict__ s,
-                                                             const float* __restrict__ w_scale,
+                                                             const float* __restrict__ w_scale, int64_t scale_step,
                                                              uint8_t* __restrict__ wq) {
     __shared__ uint32_t tile[kTN * kTStride];
     __shared__ float col_scale[kTN], col_rcp[kTN], row_s[kTJ];
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(256) void quant_weight_t_kernel(const void* __restr
     bool fast = true;
     if (threadIdx.x < kTN) {
         const int64_t n = n0 + threadIdx.x;
-        const float sc = (n < N) ? w_scale[n] : 0.0f;
+        const float sc = (n < N) ? w_scale[n * scale_step] : 0.0f;
         col_scale[threadIdx.x] = sc;
         col_rcp[threadIdx.x] = div_rn(1.0f, sc);
         fast = sc == 0.0f || in_pow2_range<-60, 60>(sc);
@@ -390,10 +390,95 @@ hipError_t quant_act_dispatch(const void* x, int64_t M, int64_t K, const float* 
 
 template <bool kBf16, bool kFp8>
 hipError_t quant_weight_dispatch(const void* w, int64_t K, int64_t N, const float* s, const float* w_scale,
-                                 uint8_t* wq, hipStream_t st) {
+                                 int64_t scale_step, uint8_t* wq, hipStream_t st) {
     dim3 grid(static_cast<unsigned>((N + kTN - 1) / kTN), static_cast<unsigned>((K + kTJ - 1) / kTJ));
-    if (N % 8 == 0) hipLaunchKernelGGL((quant_weight_t_kernel<kBf16, kFp8, true>), grid, dim3(256), 0, st, w, K, N, s, w_scale, wq);
-    else hipLaunchKernelGGL((quant_weight_t_kernel<kBf16, kFp8, false>), grid, dim3(256), 0, st, w, K, N, s, w_scale, wq);
+    if (N % 8 == 0)
+        hipLaunchKernelGGL((quant_weight_t_kernel<kBf16, kFp8, true>), grid, dim3(256), 0, st, w, K, N, s, w_scale,
+                           scale_step, wq);
+    else
+        hipLaunchKernelGGL((quant_weight_t_kernel<kBf16, kFp8, false>), grid, dim3(256), 0, st, w, K, N, s, w_scale,
+                           scale_step, wq);
+    return hipGetLastError();
+}
+
+// ---- per-tensor quantize ("Weight-Activation Quantization", s4 "Per-Tensor Scaling for FP8") ----
+//
+// One scale for the whole tensor, scale = amax_in[0] / Q, so the kernel is a plain stream of
+// 16-byte chunks: 8 elements in, 8 codes out, kU chunks in flight per thread of a grid-stride
+// loop.  Under delayed scaling amax_in is an earlier tensor's maximum and values beyond Q * scale
+// saturate; kTrack merges this tensor's maximum into amax_out in the same pass (an atomic maximum
+// per block, skipped when amax_out already holds as much).  Division: the fast exact form when the
+// scale is in [2^-60, 2^60], else the full one.  Elements are first clamped to +-2 Q scale, which
+// changes no code (both quotients saturate) and keeps the fast form's intermediates finite.
+template <bool kBf16, bool kFp8, bool kTrack>
+__global__ __launch_bounds__(256) void quant_tensor_kernel(const void* __restrict__ a, int64_t nchunk,
+                                                           const float* __restrict__ amax_in, uint8_t* __restrict__ q,
+                                                           float* __restrict__ scale_out,
+                                                           float* __restrict__ amax_out) {
+    constexpr int kU = 4;
+    const float sc = div_rn(amax_in[0], qmax<kFp8>());
+    if (blockIdx.x == 0 && threadIdx.x == 0) scale_out[0] = sc;
+    const bool fast = in_pow2_range<-60, 60>(sc);
+    const float rsc = fast ? div_rn(1.0f, sc) : 0.0f;
+    const float lim = 2.0f * qmax<kFp8>() * sc;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    float m = 0.0f;
+    for (int64_t c0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c0 < nchunk; c0 += kU * stride) {
+        Raw8<kBf16> raw[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t c = c0 + u * stride;
+            raw[u] = load_raw8<kBf16>(a, (c < nchunk ? c : nchunk - 1) * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t c = c0 + u * stride;
+            float v[8];
+            unpack8<kBf16>(raw[u], v);
+            if constexpr (kTrack) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+            }
+            if (c >= nchunk) continue;
+            uint32_t lo = 0, hi = 0;
+            if (sc != 0.0f) {                   // a zero scale gives zero codes
+                float qv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float t = fminf(fmaxf(v[e], -lim), lim);
+                    qv[e] = fast ? div_by_rcp<kFp8>(t, sc, rsc) : div_rn(t, sc);
+                }
+                lo = pack_codes4<kFp8>(qv[0], qv[1], qv[2], qv[3]);
+                hi = pack_codes4<kFp8>(qv[4], qv[5], qv[6], qv[7]);
+            }
+            *reinterpret_cast<uint2*>(q + c * 8) = make_uint2(lo, hi);
+        }
+    }
+    if constexpr (kTrack) {
+        __shared__ float part[4];
+        m = wave_max(m);
+        const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+        if (lane == 0) part[wave] = m;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const float b = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+            if (b > *amax_out) atomic_max_nonneg(amax_out, b);
+        }
+    }
+}
+
+template <bool kBf16, bool kFp8>
+hipError_t quant_tensor_dispatch(const void* a, int64_t n, const float* amax_in, uint8_t* q, float* scale_out,
+                                 float* amax_out, hipStream_t st) {
+    const int64_t nchunk = n / 8;       // n == 0: one block, which only writes the scale
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((nchunk + 256 * 4 - 1) / (256 * 4), 4096));
+    const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+    if (amax_out)
+        hipLaunchKernelGGL((quant_tensor_kernel<kBf16, kFp8, true>), grid, block, 0, st, a, nchunk, amax_in, q,
+                           scale_out, amax_out);
+    else
+        hipLaunchKernelGGL((quant_tensor_kernel<kBf16, kFp8, false>), grid, block, 0, st, a, nchunk, amax_in, q,
+                           scale_out, amax_out);
     return hipGetLastError();
 }
 
@@ -409,12 +494,22 @@ hipError_t launch_quant_act(const void* x, bool bf16, int64_t M, int64_t K, cons
 }
 
 hipError_t launch_quant_weight_t(const void* w, bool bf16, int64_t K, int64_t N, const float* s,
-                                 const float* w_scale, bool fp8, uint8_t* wq, hipStream_t st) {
+                                 const float* w_scale, bool tensor_scale, bool fp8, uint8_t* wq, hipStream_t st) {
     if (N <= 0) return hipSuccess;
-    if (bf16) return fp8 ? quant_weight_dispatch<true, true>(w, K, N, s, w_scale, wq, st)
-                         : quant_weight_dispatch<true, false>(w, K, N, s, w_scale, wq, st);
-    return fp8 ? quant_weight_dispatch<false, true>(w, K, N, s, w_scale, wq, st)
-               : quant_weight_dispatch<false, false>(w, K, N, s, w_scale, wq, st);
+    const int64_t step = tensor_scale ? 0 : 1;
+    if (bf16) return fp8 ? quant_weight_dispatch<true, true>(w, K, N, s, w_scale, step, wq, st)
+                         : quant_weight_dispatch<true, false>(w, K, N, s, w_scale, step, wq, st);
+    return fp8 ? quant_weight_dispatch<false, true>(w, K, N, s, w_scale, step, wq, st)
+               : quant_weight_dispatch<false, false>(w, K, N, s, w_scale, step, wq, st);
+}
+
+hipError_t launch_quant_tensor(const void* a, bool bf16, int64_t n, const float* amax_in, bool fp8, uint8_t* q,
+                               float* scale_out, float* amax_out, hipStream_t st) {
+    if (n < 0) return hipSuccess;
+    if (bf16) return fp8 ? quant_tensor_dispatch<true, true>(a, n, amax_in, q, scale_out, amax_out, st)
+                         : quant_tensor_dispatch<true, false>(a, n, amax_in, q, scale_out, amax_out, st);
+    return fp8 ? quant_tensor_dispatch<false, true>(a, n, amax_in, q, scale_out, amax_out, st)
+               : quant_tensor_dispatch<false, false>(a, n, amax_in, q, scale_out, amax_out, st);
 }
 
 

@@ -126,6 +126,54 @@ w8a8_status w8a8_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t M, int64_t
 w8a8_status w8a8_gemm_f32(const uint8_t* xq, const uint8_t* wq, int64_t M, int64_t N, int64_t K,
                           float* acc, hipStream_t stream);
 
+/*
+ * ---- Per-tensor scaling ([WAQ] s4 "Per-Tensor Scaling for FP8": one scale s = max|x| / 448 for a
+ * whole tensor, q = cast_fp8(x / s), x^ = s q, no smoothing; the FP8-vs-INT8 table there names
+ * delayed scaling, where s comes from the previous step's maximum.  [WAQ] s2 shows the same
+ * recipe for INT8 with 127.)  Every scale and maximum below is ONE fp32 value in device memory.
+ */
+
+/*
+ * Tensor maximum: amax[0] = max(accumulate ? amax[0] : 0, max_i |a[i]|) over n elements of a
+ * (float32 or bf16).  n >= 0 and a multiple of 8; a 16-byte aligned (else W8A8_ERR_UNSUPPORTED).
+ * Exact (no rounding), independent of how the work is split.
+ */
+w8a8_status w8a8_absmax(const void* a, w8a8_dtype dtype, int64_t n, float* amax, int accumulate,
+                        hipStream_t stream);
+
+/*
+ * Per-tensor activation quantize, one pass over X [M, K]:
+ *   x_scale[0] = amax_in[0] / Q                                (Q = 127 for INT8, 448 for E4M3)
+ *   xq[i, j]   = INT8: clamp(round_half_even(X[i, j] / x_scale[0]), -127, 127)
+ *                E4M3: e4m3_round_half_even(clamp(X[i, j] / x_scale[0], -448, 448))
+ * amax_in: this X's own maximum (from w8a8_absmax: current scaling) or an earlier step's
+ * (delayed scaling: values beyond Q * x_scale saturate).  amax_out: NULL, or a value that
+ * receives max_{i,j} |X[i, j]| in the same pass (reset first unless accumulate != 0), for the
+ * next step's amax_in; it must not be amax_in (W8A8_ERR_INVALID_ARG).  A zero amax_in gives
+ * x_scale 0 and codes 0.  xq: [M, K] bytes.  x_scale, amax_in, amax_out: 4-byte aligned.
+ */
+w8a8_status w8a8_quant_act_tensor(const void* x, w8a8_dtype x_dtype, int64_t M, int64_t K,
+                                  const float* amax_in, w8a8_qtype qtype, void* xq, float* x_scale,
+                                  float* amax_out, int accumulate, hipStream_t stream);
+
+/*
+ * Per-tensor weight quantize: w_scale[0] = max_{j,n} |W[j, n]| / Q, and
+ * wq[n, j] = the codes of W[j, n] / w_scale[0] (rounding as above), transposed to [N, K].
+ * w: [K, N] in w_dtype.  w_scale: one fp32, 4-byte aligned (it holds the running maximum
+ * divided by Q while the call runs).
+ */
+w8a8_status w8a8_quant_weight_tensor(const void* w, w8a8_dtype w_dtype, int64_t K, int64_t N,
+                                     w8a8_qtype qtype, void* wq, float* w_scale, hipStream_t stream);
+
+/*
+ * The GEMM of w8a8_gemm_dequant with one scale per operand:
+ *   y[i, n] = bf16(((float)acc[i, n] * x_scale[0]) * w_scale[0]).
+ * Same kernels, tiling and accumulation; x_scale and w_scale are single fp32 values (4-byte aligned).
+ */
+w8a8_status w8a8_gemm_dequant_tensor(const void* xq, const float* x_scale, const void* wq,
+                                     const float* w_scale, w8a8_qtype qtype, int64_t M, int64_t N,
+                                     int64_t K, void* y, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* w8a8_status_string(w8a8_status status);
 

@@ -81,6 +81,19 @@ def test_argument_validation_without_gpu():
     assert L.w8a8_gemm_dequant(None, None, None, None, 0, 0, 5, 32, None, None) == OK
     assert L.w8a8_gemm_i32(fake, fake, 4, 4, 133152, fake, None) == UNS              # int32 overflow bound
     assert L.w8a8_gemm_i32(fake, fake, 4, 4, 40, fake, None) == UNS
+    # per-tensor entry points
+    other = ctypes.c_void_p(0x200000)
+    assert L.w8a8_absmax(fake, 1, 16, None, 0, None) == INV                          # NULL amax
+    assert L.w8a8_absmax(fake, 1, 12, fake, 0, None) == UNS                          # n % 8
+    assert L.w8a8_absmax(fake, 1, -8, fake, 0, None) == INV
+    assert L.w8a8_quant_act_tensor(fake, 1, 4, 16, fake, 1, fake, other, fake, 0, None) == INV  # amax_out is amax_in
+    assert L.w8a8_quant_act_tensor(fake, 1, 4, 16, None, 1, fake, other, None, 0, None) == INV  # NULL amax_in
+    assert L.w8a8_quant_act_tensor(fake, 1, 4, 24, fake, 1, fake, other, None, 0, None) == UNS  # K % 16
+    assert L.w8a8_quant_act_tensor(fake, 1, 4, 16, fake, 3, fake, other, None, 0, None) == INV  # bad qtype
+    assert L.w8a8_quant_weight_tensor(fake, 1, 16, 8, 1, fake, None, None) == INV    # NULL w_scale
+    assert L.w8a8_quant_weight_tensor(odd, 1, 16, 8, 1, fake, other, None) == UNS    # alignment
+    assert L.w8a8_gemm_dequant_tensor(fake, fake, fake, fake, 1, 4, 4, 32, None, None) == INV
+    assert L.w8a8_gemm_dequant_tensor(None, None, None, None, 1, 4, 0, 32, None, None) == OK
 
 
 def test_product_path_does_not_touch_the_oracle():
