@@ -227,7 +227,10 @@ hipError_t launch_absmax_rows(const void* a, bool bf16, int64_t R, int64_t C, fl
 hipError_t launch_absmax_tensor(const void* a, bool bf16, int64_t n, float divisor, float* out, hipStream_t st) {
     if (n <= 0) return hipSuccess;
     const int64_t nchunk = n / 8;
-    const int64_t blocks = std::min<int64_t>((nchunk + 256 * 8 - 1) / (256 * 8), 4096);
+    // At most 1024 blocks: every block ends with one atomic on the same address, and blocks that
+    // finish together queue behind each other there (4096 blocks over a freshly zeroed maximum
+    // doubled the time of a 134 MB pass).
+    const int64_t blocks = std::min<int64_t>((nchunk + 256 * 8 - 1) / (256 * 8), 1024);
     if (bf16)
         hipLaunchKernelGGL(absmax_tensor_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a, nchunk,
                            divisor, out);

@@ -21,6 +21,7 @@ pytestmark = pytest.mark.gpu
 def native_library():
     import fp8_gemm_amd
     assert torch.cuda.is_available(), "GPU tests need a GPU"
+    fp8_gemm_amd.w8a8_version()                  # loads the library
     assert fp8_gemm_amd.lib_path() in open("/proc/self/maps").read(), "libw8a8.so is not loaded"
     yield fp8_gemm_amd
 
