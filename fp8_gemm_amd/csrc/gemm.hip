@@ -733,37 +733,42 @@ hipError_t gemm_dispatch(const uint8_t* xq, const float* x_scale, const uint8_t*
                            st, xq, x_scale, wq, w_scale, M, N, K, y, out_acc, tensor);
         return hipGetLastError();
     }
-    if (M <= 64) {
+    if (M <= 16 || (M <= 32 && N <= 8192)) {
+        // A block per 16 output columns streams W once; X is re-read per block from L2, which is
+        // cheap while M and N are small.
         dim3 grid(static_cast<unsigned>((N + 15) / 16));
         if (M <= 16)
             hipLaunchKernelGGL((gemm_small_m_kernel<1, M16, kOutAcc>), grid, dim3(kThreads), 0, st, xq, x_scale, wq,
                                w_scale, M, N, K, y, out_acc, tensor);
-        else if (M <= 32)
-            hipLaunchKernelGGL((gemm_small_m_kernel<2, M16, kOutAcc>), grid, dim3(kThreads), 0, st, xq, x_scale, wq,
-                               w_scale, M, N, K, y, out_acc, tensor);
         else
-            hipLaunchKernelGGL((gemm_small_m_kernel<4, M16, kOutAcc>), grid, dim3(kThreads), 0, st, xq, x_scale, wq,
+            hipLaunchKernelGGL((gemm_small_m_kernel<2, M16, kOutAcc>), grid, dim3(kThreads), 0, st, xq, x_scale, wq,
                                w_scale, M, N, K, y, out_acc, tensor);
         return hipGetLastError();
     }
+    // Tiles: the largest tile that still gives at least kFill tiles (about three quarters of the 256
+    // CUs, one tile each); with fewer, a CU's per-tile K loop is the whole kernel's time, so smaller
+    // tiles finish sooner.  The smallest (64 x 64) is the fallback.
+    constexpr int64_t kFill = 192;
     const int group_m = 4;
-    const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-    if (big_tiles >= 512) {
+    auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    auto launch = [&](auto kernel, int bm, int bn, int threads) {
+        const int tiles_m = static_cast<int>((M + bm - 1) / bm);
+        const int tiles_n = static_cast<int>((N + bn - 1) / bn);
+        hipLaunchKernelGGL(kernel, dim3(tiles_m * tiles_n), dim3(threads), 0, st, xq, x_scale, wq, w_scale, M, N, K, y,
+                           out_acc, tiles_m, tiles_n, group_m, tensor);
+    };
+    if (tiles(256, 256) >= 512) {
         // Enough 256 x 256 tiles for two rounds over 256 CUs: 4 waves of 128 x 128 outputs, half the
         // LDS reads and two thirds of the copies per matrix-core instruction of the smaller tile.
-        constexpr int kBM = 256, kBN = 256, kGM = 2, kGN = 2;
-        const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
-        const int tiles_n = static_cast<int>((N + kBN - 1) / kBN);
-        hipLaunchKernelGGL((gemm_tile_kernel<kBM, kBN, kGM, kGN, 2, 1, MT, kOutAcc>), dim3(tiles_m * tiles_n),
-                           dim3(kGM * kGN * kWave), 0, st, xq, x_scale, wq, w_scale, M, N, K, y, out_acc, tiles_m,
-                           tiles_n, group_m, tensor);
+        launch(gemm_tile_kernel<256, 256, 2, 2, 2, 1, MT, kOutAcc>, 256, 256, 4 * kWave);
+    } else if (tiles(256, 128) >= kFill) {
+        launch(gemm_tile_kernel<256, 128, 4, 2, 3, 2, MT, kOutAcc>, 256, 128, 8 * kWave);
+    } else if (tiles(128, 128) >= kFill) {
+        launch(gemm_tile_kernel<128, 128, 2, 2, 3, 1, MT, kOutAcc>, 128, 128, 4 * kWave);
+    } else if (tiles(64, 128) >= kFill) {
+        launch(gemm_tile_kernel<64, 128, 1, 4, 3, 1, MT, kOutAcc>, 64, 128, 4 * kWave);
     } else {
-        constexpr int kBM = 256, kBN = 128, kGM = 4, kGN = 2;
-        const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
-        const int tiles_n = static_cast<int>((N + kBN - 1) / kBN);
-        hipLaunchKernelGGL((gemm_tile_kernel<kBM, kBN, kGM, kGN, 3, 2, MT, kOutAcc>), dim3(tiles_m * tiles_n),
-                           dim3(kGM * kGN * kWave), 0, st, xq, x_scale, wq, w_scale, M, N, K, y, out_acc, tiles_m,
-                           tiles_n, group_m, tensor);
+        launch(gemm_tile_kernel<64, 64, 2, 2, 3, 1, MT, kOutAcc>, 64, 64, 4 * kWave);
     }
     return hipGetLastError();
 }

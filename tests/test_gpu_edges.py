@@ -82,7 +82,23 @@ def test_big_tile_shapes(f, qtype, M, K, N):
     """Shapes with at least 512 tiles of 256 x 256 outputs take the two-stage 256 x 256 kernel: ragged
     M, N and K (a partial last K step) with several steady-state K steps.  Codes and scales in full;
     accumulators (INT8) and outputs on 64 sampled rows, including the first and the last."""
-    announce(f"big tiles M={M} K={K} N={N} {qtype}")
+    check_sampled_rows(f, qtype, M, K, N)
+
+
+# (M, K, N) for each tile size below 256 x 256 (the largest with at least 192 tiles), all ragged:
+# 256 x 128 (217 tiles), 128 x 128 (192), 64 x 128 (192), and 64 x 64 with N too large for the
+# small-M kernel at M = 24.
+TILE_SHAPES = [(1700, 400, 3900), (1000, 528, 3000), (380, 272, 4090), (24, 1040, 9000)]
+
+
+@pytest.mark.parametrize("M,K,N", TILE_SHAPES)
+@pytest.mark.parametrize("qtype", ["int8", "fp8"])
+def test_tile_configs(f, qtype, M, K, N):
+    check_sampled_rows(f, qtype, M, K, N)
+
+
+def check_sampled_rows(f, qtype, M, K, N):
+    announce(f"sampled rows M={M} K={K} N={N} {qtype}")
     X = synth.random_matrix((M, K), seed=M + K, dtype="bf16", outliers=max(1, K // 100))
     W = synth.random_matrix((K, N), seed=N + K, dtype="bf16", scale=0.02)
     x, w = dev(X), dev(W)
@@ -98,7 +114,7 @@ def test_big_tile_shapes(f, qtype, M, K, N):
     qw, sw_ref = oracle.fold_quant_weight(W, s_ref, qtype)
     np.testing.assert_array_equal(host(xq).view(np.uint8), qx.view(np.uint8))
     np.testing.assert_array_equal(host(wq).view(np.uint8), qw.view(np.uint8))
-    rows = np.unique(np.concatenate([[0, M - 1], np.random.Generator(np.random.PCG64(K)).choice(M, 62, replace=False)]))
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.Generator(np.random.PCG64(K)).choice(M, min(M, 62), replace=False)]))
     yg = host(y)[rows]
     if qtype == "int8":
         a = oracle.gemm_i32(qx[rows], qw)
