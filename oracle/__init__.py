@@ -57,6 +57,7 @@ def _load():
         "oracle_tensor_scale": (F, [F, I]),
         "oracle_quantize_tensor": (None, [P, I, I64, F, I, P]),
         "oracle_quant_weight_tensor": (I, [P, I, I64, I64, I, P, P]),
+        "oracle_gemm_w8a16": (I, [P, I, P, P, I64, I64, I64, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -340,3 +341,21 @@ def layer_tensor(x, w, qtype="fp8", amax_x=None):
         y64, mag = gemm_fp8(qx, qw, sxv, swv)
         out.update(y64=y64, mag64=mag)
     return out
+
+
+# --- weight-only W8A16 GEMM (Weight-Activation Quantization, s1; the W8A16-vs-W8A8 lesson) ----
+
+def gemm_w8a16(x, q, sw):
+    """16-bit X [M, K] times dequantized INT8 weights (q [N, K], per-channel sw [N]):
+    returns (y64, mag64), both float64 [M, N]; y64 = sw[n] * sum_k x[m, k] q[n, k]."""
+    lib = _load()
+    x, dt = _input(x)
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    M, K = x.shape
+    N, K2 = q.shape
+    assert K == K2
+    y64 = np.empty((M, N), np.float64)
+    mag = np.empty((M, N), np.float64)
+    if lib.oracle_gemm_w8a16(_ptr(x), dt, _ptr(q), _ptr(_f32(sw)), M, N, K, _ptr(y64), _ptr(mag)) != 0:
+        raise MemoryError("oracle_gemm_w8a16")
+    return y64, mag

@@ -32,7 +32,9 @@
  *   - E4M3 is the OCP "fn" flavour: bias 7, largest finite 448, subnormals m * 2^-9, no
  *     infinities; values are clamped to [-448, 448] before rounding;
  *   - per-tensor scaling (s4) uses one scale max|x| / Q for a whole tensor, without smoothing;
- *     under delayed scaling the maximum is an earlier tensor's, and values beyond Q * s saturate.
+ *     under delayed scaling the maximum is an earlier tensor's, and values beyond Q * s saturate;
+ *   - W8A16 (weight-only) multiplies 16-bit X by q * sw; the per-channel scale factors out of the
+ *     sum, and the reference is that sum in double (the dequantized weight is not rounded first).
  *
  * Arithmetic: IEEE binary32/binary64, round-to-nearest-even, compiled without fast-math and
  * without FMA contraction.  Every loop is the definition written out; the only parallelism is an
@@ -370,5 +372,40 @@ int oracle_quant_weight_tensor(const void* w, int dtype, int64_t K, int64_t N, i
         for (int64_t n = 0; n < N; ++n) q[n * K + j] = t[j * N + n];
     *scale = sc;
     free(t);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Weight-only W8A16 GEMM, the contrast the pages draw with W8A8 ([WAQ] s1 "Why Quantize
+ * Activations Too?": weight-only quantization keeps the GEMM in 16-bit with one low-precision
+ * operand; the W8A16-vs-W8A8 lesson, s1: the 8-bit weights are dequantized to 16-bit on the fly
+ * and the multiply runs on 16-bit tensor cores).  The weights are per-output-channel INT8 codes
+ * q [N, K] with scales sw [N] (the weight quantize of s2 without smoothing); X stays 16-bit.  The
+ * dequantized weight q[n, k] * sw[n] has one scale per output channel, which factors out of the
+ * sum over k:
+ *   y64[m, n]   = sw[n] * sum_k x[m, k] * q[n, k]      (double; every product is exact)
+ *   mag64[m, n] = sw[n] * sum_k |x[m, k] * q[n, k]|    (for a floating-point error bound)
+ * ------------------------------------------------------------------------------------------- */
+int oracle_gemm_w8a16(const void* x, int dtype, const int8_t* q, const float* sw, int64_t M, int64_t N, int64_t K,
+                      double* y64, double* mag64) {
+    double* xd = (double*)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
+    if (!xd) return -1;
+    for (int64_t i = 0; i < M * K; ++i) xd[i] = (double)load_elem(x, dtype, i);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        const double* a = xd + m * K;
+        for (int64_t n = 0; n < N; ++n) {
+            const int8_t* b = q + n * K;
+            double t = 0.0, u = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double p = a[k] * (double)b[k];
+                t += p;
+                u += fabs(p);
+            }
+            if (y64) y64[m * N + n] = t * (double)sw[n];
+            if (mag64) mag64[m * N + n] = u * (double)sw[n];
+        }
+    }
+    free(xd);
     return 0;
 }

@@ -1,7 +1,8 @@
 """Pins of the oracle's per-tensor scaling ("Weight-Activation Quantization", s4 "Per-Tensor
-Scaling for FP8", and the per-tensor INT8 example of s2) against things other than itself: the
-page's outlier row, library routines with the same semantics (numpy float32 division and
-round-half-even, torch's float8_e4m3fn cast), closed forms and invariants.
+Scaling for FP8", and the per-tensor INT8 example of s2) and of its weight-only W8A16 GEMM (s1 and
+the W8A16-vs-W8A8 lesson) against things other than themselves: the page's outlier row, library
+routines with the same semantics (numpy float32 division and round-half-even, torch's
+float8_e4m3fn cast, numpy float64 matmul), closed forms and invariants.
 
 Each test names the kind of mistake it is there to catch.
 """
@@ -175,3 +176,41 @@ def test_layer_tensor_fp8_dequant_closed_form():
     dw = np.vectorize(oracle.e4m3_decode)(out["qw"]).astype(np.float64)
     brute = (dx @ dw.T) * float(out["sx"]) * float(out["sw"])
     np.testing.assert_allclose(out["y64"], brute, rtol=1e-15, atol=0)
+
+
+# ---------------------------------------------------------------------------------------------
+# Weight-only W8A16 (Weight-Activation Quantization, s1; the W8A16-vs-W8A8 lesson, s1)
+# ---------------------------------------------------------------------------------------------
+
+def test_w8a16_matches_numpy_dequantized_matmul():
+    """y = X (q sw)^T with the dequantized weights, numpy float64 matmul.  Catches: the scale on the
+    wrong axis, codes transposed, bf16 X read as something else."""
+    X = synth.f32_to_bf16_bits(synth.random_matrix((9, 200), seed=31, outliers=2))
+    W = synth.random_matrix((200, 13), seed=32, scale=0.02)
+    q, sw = oracle.fold_quant_weight(W, None, "int8")
+    y64, mag = oracle.gemm_w8a16(X, q, sw)
+    Wd = q.astype(np.float64) * sw.astype(np.float64)[:, None]           # [N, K] dequantized
+    ref = synth.bf16_bits_to_f32(X).astype(np.float64) @ Wd.T
+    np.testing.assert_allclose(y64, ref, rtol=1e-12, atol=1e-300)
+    absref = np.abs(synth.bf16_bits_to_f32(X).astype(np.float64)) @ np.abs(Wd).T
+    np.testing.assert_allclose(mag, absref, rtol=1e-12, atol=1e-300)
+
+
+def test_w8a16_one_hot_rows_and_integer_inputs():
+    """One-hot rows of X pick single dequantized weights exactly; integer X gives sw times the
+    integer GEMM exactly.  Catches: a dropped scale, an off-by-one in k."""
+    K, N = 64, 5
+    q = synth.random_codes((N, K), seed=33)
+    sw = synth.random_scales(N, seed=34)
+    X = np.zeros((3, K), np.float32)
+    X[0, 0] = 1.0
+    X[1, 17] = 1.0
+    X[2, K - 1] = -2.0
+    y64, _ = oracle.gemm_w8a16(X, q, sw)
+    np.testing.assert_array_equal(y64[0], q[:, 0].astype(np.float64) * sw.astype(np.float64))
+    np.testing.assert_array_equal(y64[1], q[:, 17].astype(np.float64) * sw.astype(np.float64))
+    np.testing.assert_array_equal(y64[2], -2.0 * q[:, K - 1].astype(np.float64) * sw.astype(np.float64))
+    Xi = np.random.Generator(np.random.PCG64(35)).integers(-127, 128, (7, K)).astype(np.float32)
+    y64, _ = oracle.gemm_w8a16(Xi, q, sw)
+    acc = oracle.gemm_i32(Xi.astype(np.int8), q)
+    np.testing.assert_array_equal(y64, acc.astype(np.float64) * sw.astype(np.float64)[None, :])
