@@ -26,7 +26,8 @@ W8A8_INT8, W8A8_FP8_E4M3 = 0, 1
 
 ENTRY_POINTS = ("w8a8_smooth_scales", "w8a8_fold_quant_weight", "w8a8_quant_act", "w8a8_gemm_dequant",
                 "w8a8_gemm_i32", "w8a8_gemm_f32", "w8a8_absmax", "w8a8_quant_act_tensor",
-                "w8a8_quant_weight_tensor", "w8a8_gemm_dequant_tensor", "w8a8_status_string", "w8a8_version")
+                "w8a8_quant_weight_tensor", "w8a8_gemm_dequant_tensor", "w8a8_gemm_w8a16", "w8a8_status_string",
+                "w8a8_version")
 
 
 class W8A8Error(RuntimeError):
@@ -57,6 +58,7 @@ def _load() -> ctypes.CDLL:
         "w8a8_quant_act_tensor": (I, [P, I, I64, I64, P, I, P, P, P, I, P]),
         "w8a8_quant_weight_tensor": (I, [P, I, I64, I64, I, P, P, P]),
         "w8a8_gemm_dequant_tensor": (I, [P, P, P, P, I, I64, I64, I64, P, P]),
+        "w8a8_gemm_w8a16": (I, [P, P, P, I64, I64, I64, P, P]),
         "w8a8_status_string": (ctypes.c_char_p, [I]),
         "w8a8_version": (ctypes.c_char_p, []),
     }
@@ -282,3 +284,22 @@ def w8a8_layer_tensor(x, w, qtype="fp8", amax_prev=None, stream=None):
         xq, x_scale, amax = w8a8_quant_act_tensor(x, amax_prev, qtype, track=True, stream=stream)
     y = w8a8_gemm_dequant_tensor(xq, x_scale, wq, w_scale, qtype, stream=stream)
     return dict(wq=wq, w_scale=w_scale, xq=xq, x_scale=x_scale, amax=amax, y=y)
+
+
+# ---- weight-only W8A16 ------------------------------------------------------------------------------
+
+def w8a8_gemm_w8a16(x, wq, w_scale, y=None, stream=None):
+    """bf16 X [M, K] times INT8 weights (wq [N, K], per-channel w_scale [N]) on the bf16 matrix
+    cores: Y bfloat16 [M, N] = w_scale[n] * sum_k x[m, k] wq[n, k]."""
+    for t, n in ((x, "x"), (wq, "wq"), (w_scale, "w_scale")):
+        _dev(t, n)
+    if x.dtype != torch.bfloat16 or wq.dtype != torch.int8:
+        raise TypeError("w8a8_gemm_w8a16 takes bf16 x and int8 wq")
+    M, K = x.shape
+    N, K2 = wq.shape
+    if K2 != K:
+        raise ValueError("x is [M, K] and wq is [N, K]")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else _dev(y, "y")
+    _check("w8a8_gemm_w8a16", _load().w8a8_gemm_w8a16(_ptr(x), _ptr(wq), _ptr(w_scale), M, N, K, _ptr(y),
+                                                      _stream(stream)))
+    return y

@@ -189,6 +189,19 @@ W8A8_API w8a8_status w8a8_gemm_dequant_tensor(const void* xq, const float* x_sca
                                       nullptr, stream));
 }
 
+// ---- weight-only W8A16 ------------------------------------------------------------------------------
+
+W8A8_API w8a8_status w8a8_gemm_w8a16(const void* x, const int8_t* wq, const float* w_scale, int64_t M, int64_t N,
+                                     int64_t K, void* y, hipStream_t stream) {
+    if (M > 0 && N > 0 && (!x || !wq || !w_scale || !y)) return W8A8_ERR_INVALID_ARG;
+    w8a8_status st = check_dims(M, N, K);
+    if (st != W8A8_OK) return st;
+    if (M == 0 || N == 0) return W8A8_OK;
+    if (!aligned16(x) || !aligned16(wq) || !aligned16(y) || !aligned16(w_scale)) return W8A8_ERR_UNSUPPORTED;
+    return from_hip(w8a8::launch_gemm_w8a16(static_cast<const uint16_t*>(x), wq, w_scale, M, N, K,
+                                            static_cast<uint16_t*>(y), stream));
+}
+
 W8A8_API const char* w8a8_status_string(w8a8_status status) {
     switch (status) {
         case W8A8_OK: return "ok";

@@ -180,4 +180,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
 }
 
+// Store a block's bf16 output tiles t = t0, t0 + G, ... (rows m < M <= 16, 16 columns each) from
+// LDS: ybuf[j] holds tile t0 + j G.  16-byte stores where the row allows them.
+__device__ __forceinline__ void store_tiles_bf16(const uint16_t (*ybuf)[16][16], int ntiles_block, int t0, int G,
+                                            int64_t M, int64_t N, uint16_t* __restrict__ y) {
+    const int rows = static_cast<int>(M);
+    const bool vec_ok = (N % 8) == 0;
+    for (int i = threadIdx.x; i < ntiles_block * rows * 2; i += blockDim.x) {
+        const int j = i / (rows * 2), m = (i / 2) % rows, h = i % 2;
+        const int64_t n = (static_cast<int64_t>(t0) + static_cast<int64_t>(j) * G) * 16 + 8 * h;
+        const uint4 v = *reinterpret_cast<const uint4*>(&ybuf[j][m][8 * h]);
+        uint16_t* dst = y + m * N + n;
+        if (vec_ok && n + 7 < N) {
+            *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (n + e < N) dst[e] = static_cast<uint16_t>(w4[e / 2] >> (16 * (e % 2)));
+        }
+    }
+}
+
 }  // namespace w8a8

@@ -174,6 +174,20 @@ w8a8_status w8a8_gemm_dequant_tensor(const void* xq, const float* x_scale, const
                                      const float* w_scale, w8a8_qtype qtype, int64_t M, int64_t N,
                                      int64_t K, void* y, hipStream_t stream);
 
+/*
+ * ---- Weight-only W8A16, the contrast the pages draw with W8A8 ([WAQ] s1 "Why Quantize Activations
+ * Too?": weight-only quantization keeps the GEMM in 16-bit; the W8A16-vs-W8A8 lesson, s1: the 8-bit
+ * weights are dequantized to 16-bit on the fly and the multiply runs on 16-bit tensor cores).
+ *   y[i, n] = bf16(w_scale[n] * sum_k x[i, k] * wq[n, k])
+ * x: bf16 [M, K] (not quantized).  wq: int8 [N, K] and w_scale: fp32 [N], the per-output-channel
+ * codes and scales of w8a8_fold_quant_weight (with s == NULL for plain weight-only quantization).
+ * The codes are converted to bf16 exactly (|q| <= 127), multiplied on the bf16 matrix cores with
+ * fp32 accumulation (products exact, summation order the hardware's), and the channel scale is
+ * applied to the sum (the dequantized weight q * w_scale factors out of it).  y: bf16 [M, N].
+ */
+w8a8_status w8a8_gemm_w8a16(const void* x, const int8_t* wq, const float* w_scale, int64_t M, int64_t N,
+                            int64_t K, void* y, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* w8a8_status_string(w8a8_status status);
 
