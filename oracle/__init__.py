@@ -58,6 +58,9 @@ def _load():
         "oracle_quantize_tensor": (None, [P, I, I64, F, I, P]),
         "oracle_quant_weight_tensor": (I, [P, I, I64, I64, I, P, P]),
         "oracle_gemm_w8a16": (I, [P, I, P, P, I64, I64, I64, P, P]),
+        "oracle_fold_norm_gain": (None, [P, P, I64, P]),
+        "oracle_rms_norm": (None, [P, I, I64, I64, P, F, P]),
+        "oracle_norm_quant_act": (I, [P, I, I64, I64, P, F, I, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -359,3 +362,36 @@ def gemm_w8a16(x, q, sw):
     if lib.oracle_gemm_w8a16(_ptr(x), dt, _ptr(q), _ptr(_f32(sw)), M, N, K, _ptr(y64), _ptr(mag)) != 0:
         raise MemoryError("oracle_gemm_w8a16")
     return y64, mag
+
+
+# --- smoothing folded into the norm before the layer (s3 step 1, offline; the lesson's s2) ----
+
+def fold_norm_gain(g, s):
+    """g'[j] = g[j] / s[j] (g None: 1), float32 [K]."""
+    K = len(s) if s is not None else len(g)
+    out = np.empty(K, np.float32)
+    _load().oracle_fold_norm_gain(_ptr(_f32(g)), _ptr(_f32(s)), K, _ptr(out))
+    return out
+
+
+def rms_norm(h, g=None, eps=1e-5):
+    """(h[j] * r) * g[j] per row, r = 1 / sqrt(mean(h^2) + eps): float32 [M, K]."""
+    h, dt = _input(h)
+    M, K = h.shape
+    out = np.empty((M, K), np.float32)
+    _load().oracle_rms_norm(_ptr(h), dt, M, K, _ptr(_f32(g)), float(np.float32(eps)), _ptr(out))
+    return out
+
+
+def norm_quant_act(h, g=None, eps=1e-5, qtype="int8"):
+    """RMS norm with gain g (1/s folded in), then per-token quantize: (codes [M, K], scales [M])."""
+    lib = _load()
+    q = qtype_code(qtype)
+    h, dt = _input(h)
+    M, K = h.shape
+    codes = np.empty((M, K), np.uint8)
+    sx = np.empty(M, np.float32)
+    if lib.oracle_norm_quant_act(_ptr(h), dt, M, K, _ptr(_f32(g)), float(np.float32(eps)), q, _ptr(codes),
+                                 _ptr(sx)) != 0:
+        raise MemoryError("oracle_norm_quant_act")
+    return _codes(codes, q), sx

@@ -34,7 +34,10 @@
  *   - per-tensor scaling (s4) uses one scale max|x| / Q for a whole tensor, without smoothing;
  *     under delayed scaling the maximum is an earlier tensor's, and values beyond Q * s saturate;
  *   - W8A16 (weight-only) multiplies 16-bit X by q * sw; the per-channel scale factors out of the
- *     sum, and the reference is that sum in double (the dequantized weight is not rounded first).
+ *     sum, and the reference is that sum in double (the dequantized weight is not rounded first);
+ *   - with the smoothing folded offline into the layer before, that layer is an RMS norm
+ *     (x * r) * g with r = 1 / sqrt(mean(x^2) + eps), the mean taken in double and rounded to
+ *     float once, and 1/s folded into its gain g' = g / s.
  *
  * Arithmetic: IEEE binary32/binary64, round-to-nearest-even, compiled without fast-math and
  * without FMA contraction.  Every loop is the definition written out; the only parallelism is an
@@ -407,5 +410,48 @@ int oracle_gemm_w8a16(const void* x, int dtype, const int8_t* q, const float* sw
         }
     }
     free(xd);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * The activation step with the smoothing folded into the layer before it ([WAQ] s3 step 1: the
+ * SmoothQuant transform is done offline, during model preparation; the W8A16-vs-W8A8 lesson, s2:
+ * the whole process happens offline, with no runtime overhead).  X is the output of an RMS norm
+ * of the residual stream h (the norm of the Llama models the pages name), and 1/s is folded into
+ * the norm's gain once, offline:
+ *   g'[j] = g[j] / s[j]                                     (fp32 division)
+ * then per row of h [M, K]:
+ *   ms    = (float)((sum_j (double)h[j] * h[j]) / K)        (sum in double, rounded once)
+ *   r     = 1 / sqrtf(ms + eps)                             (fp32 add, correctly rounded root, division)
+ *   X~[j] = (h[j] * r) * g'[j]                              (fp32, two roundings, in this order)
+ * and X~ is quantized per row as in oracle_quantize_rows.  g == NULL: g = 1.
+ * ------------------------------------------------------------------------------------------- */
+void oracle_fold_norm_gain(const float* g, const float* s, int64_t K, float* gout) {
+    for (int64_t j = 0; j < K; ++j) gout[j] = (g ? g[j] : 1.0f) / (s ? s[j] : 1.0f);
+}
+
+void oracle_rms_norm(const void* h, int dtype, int64_t M, int64_t K, const float* g, float eps, float* out) {
+    for (int64_t m = 0; m < M; ++m) {
+        double ss = 0.0;
+        for (int64_t j = 0; j < K; ++j) {
+            const double v = (double)load_elem(h, dtype, m * K + j);
+            ss += v * v;
+        }
+        const float ms = (float)(ss / (double)K);
+        const float r = 1.0f / sqrtf(ms + eps);
+        for (int64_t j = 0; j < K; ++j) {
+            const float v = load_elem(h, dtype, m * K + j);
+            out[m * K + j] = (v * r) * (g ? g[j] : 1.0f);
+        }
+    }
+}
+
+int oracle_norm_quant_act(const void* h, int dtype, int64_t M, int64_t K, const float* g, float eps, int qtype,
+                          uint8_t* q, float* sx) {
+    float* xs = (float*)malloc(sizeof(float) * (size_t)(M * K > 0 ? M * K : 1));
+    if (!xs) return -1;
+    oracle_rms_norm(h, dtype, M, K, g, eps, xs);
+    oracle_quantize_rows(xs, M, K, qtype, q, sx);
+    free(xs);
     return 0;
 }

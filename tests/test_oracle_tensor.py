@@ -1,6 +1,7 @@
 """Pins of the oracle's per-tensor scaling ("Weight-Activation Quantization", s4 "Per-Tensor
-Scaling for FP8", and the per-tensor INT8 example of s2) and of its weight-only W8A16 GEMM (s1 and
-the W8A16-vs-W8A8 lesson) against things other than themselves: the page's outlier row, library
+Scaling for FP8", and the per-tensor INT8 example of s2), of its weight-only W8A16 GEMM (s1 and
+the W8A16-vs-W8A8 lesson) and of its RMS norm with the smoothing folded into the gain (s3 step 1,
+offline) against things other than themselves: the page's outlier row, library
 routines with the same semantics (numpy float32 division and round-half-even, torch's
 float8_e4m3fn cast, numpy float64 matmul), closed forms and invariants.
 
@@ -214,3 +215,70 @@ def test_w8a16_one_hot_rows_and_integer_inputs():
     y64, _ = oracle.gemm_w8a16(Xi, q, sw)
     acc = oracle.gemm_i32(Xi.astype(np.int8), q)
     np.testing.assert_array_equal(y64, acc.astype(np.float64) * sw.astype(np.float64)[None, :])
+
+
+# ---------------------------------------------------------------------------------------------
+# Smoothing folded into the norm before the layer (s3 step 1 offline; the lesson's s2)
+# ---------------------------------------------------------------------------------------------
+
+def rms_ref(h64, g64, eps):
+    return h64 / np.sqrt(np.mean(h64 * h64, axis=1, keepdims=True) + eps) * g64[None, :]
+
+
+def test_rms_norm_matches_numpy_float64():
+    """Within a few fp32 roundings of the float64 formula.  Catches: mean over the wrong axis, a
+    missing eps, sum instead of mean, the gain on the wrong axis."""
+    h = synth.random_matrix((11, 320), seed=41, outliers=3)
+    g = synth.random_scales(320, seed=42, lo=0.5, hi=2.0)
+    for eps in (1e-5, 0.0):
+        y = oracle.rms_norm(h, g, eps)
+        ref = rms_ref(h.astype(np.float64), g.astype(np.float64), eps)
+        np.testing.assert_allclose(y, ref, rtol=4e-7, atol=0)
+
+
+def test_rms_norm_exact_cases():
+    """Closed forms: a constant row 4 gives r = 1/4 exactly, so X~ = g; scaling a row by a power of
+    two (eps = 0) leaves the output bit-identical.  Catches: rounding the wrong quantity, rms of
+    something other than h."""
+    g = synth.random_scales(64, seed=43, lo=0.5, hi=2.0)
+    h = np.full((1, 64), 4.0, np.float32)
+    np.testing.assert_array_equal(oracle.rms_norm(h, g, 0.0)[0], g)
+    h = synth.random_matrix((5, 64), seed=44, outliers=1)
+    y = oracle.rms_norm(h, g, 0.0)
+    for k in (-3, 5):
+        np.testing.assert_array_equal(oracle.rms_norm(h * np.float32(2.0 ** k), g, 0.0), y)
+
+
+def test_fold_norm_gain_divides_and_identity_holds():
+    """g' = g / s (one fp32 division); with it the norm output equals the smoothed norm output to
+    fp32 rounding, and (norm(h) g / s) (s W) equals norm(h) g W (the SmoothQuant identity of s3).
+    Catches: multiplying by s, folding into the wrong side."""
+    K, N = 96, 7
+    g = synth.random_scales(K, seed=45, lo=0.5, hi=2.0)
+    s = synth.random_scales(K, seed=46, lo=0.1, hi=8.0)
+    gf = oracle.fold_norm_gain(g, s)
+    np.testing.assert_array_equal(gf, (g / s).astype(np.float32))
+    h = synth.random_matrix((9, K), seed=47, outliers=2)
+    W = synth.random_matrix((K, N), seed=48, scale=0.02)
+    xs = oracle.rms_norm(h, gf, 1e-5).astype(np.float64)
+    x = oracle.rms_norm(h, g, 1e-5).astype(np.float64)
+    np.testing.assert_allclose(xs, x / s.astype(np.float64)[None, :], rtol=5e-7, atol=0)
+    ws = oracle.smooth_weight(W, s).astype(np.float64)
+    ref = x @ W.astype(np.float64)
+    assert np.linalg.norm(xs @ ws - ref) <= 1e-5 * np.linalg.norm(ref)
+
+
+def test_norm_quant_act_is_norm_then_per_row_quantize():
+    """The codes and scales are the per-row quantize of the normalized row (numpy float32 division
+    and round-half-even for INT8, torch's E4M3 cast for FP8)."""
+    h = synth.f32_to_bf16_bits(synth.random_matrix((13, 256), seed=49, outliers=2))
+    g = synth.random_scales(256, seed=50, lo=0.5, hi=2.0)
+    y = oracle.rms_norm(h, g, 1e-5)
+    amax = np.max(np.abs(y), axis=1)
+    for qt in ("int8", "fp8"):
+        q, sx = oracle.norm_quant_act(h, g, 1e-5, qt)
+        Q = np.float32(127 if qt == "int8" else 448)
+        np.testing.assert_array_equal(sx, (amax / Q).astype(np.float32))
+        for r in range(13):
+            ref = int8_ref(y[r], sx[r]) if qt == "int8" else e4m3_ref(y[r], sx[r])
+            np.testing.assert_array_equal(q[r], ref)
