@@ -421,23 +421,36 @@ int oracle_gemm_w8a16(const void* x, int dtype, const int8_t* q, const float* sw
  * the norm's gain once, offline:
  *   g'[j] = g[j] / s[j]                                     (fp32 division)
  * then per row of h [M, K]:
- *   ms    = (float)((sum_j (double)h[j] * h[j]) / K)        (sum in double, rounded once)
+ *   ms    = (float)((sum_j (double)h[j] * h[j]) / K)        (the sum carried in double-double)
  *   r     = 1 / sqrtf(ms + eps)                             (fp32 add, correctly rounded root, division)
  *   X~[j] = (h[j] * r) * g'[j]                              (fp32, two roundings, in this order)
  * and X~ is quantized per row as in oracle_quantize_rows.  g == NULL: g = 1.
+ * The sum of squares (each square of a float is exact in double) is carried as an unevaluated
+ * pair hi + lo with error-free additions (Knuth's TwoSum), so it is within about 2^-100 of the
+ * exact sum whatever the order of the terms; rounded to double and divided by K, it gives a mean
+ * that any summation order reproduces after the rounding to float.
  * ------------------------------------------------------------------------------------------- */
+/* (hi, lo) + x for |lo| <= ulp(hi) / 2: TwoSum, then renormalization. */
+static void dd_add(double* hi, double* lo, double x) {
+    const double s = *hi + x;
+    const double bb = s - *hi;
+    const double e = (*hi - (s - bb)) + (x - bb) + *lo;
+    *hi = s + e;
+    *lo = e - (*hi - s);
+}
+
 void oracle_fold_norm_gain(const float* g, const float* s, int64_t K, float* gout) {
     for (int64_t j = 0; j < K; ++j) gout[j] = (g ? g[j] : 1.0f) / (s ? s[j] : 1.0f);
 }
 
 void oracle_rms_norm(const void* h, int dtype, int64_t M, int64_t K, const float* g, float eps, float* out) {
     for (int64_t m = 0; m < M; ++m) {
-        double ss = 0.0;
+        double hi = 0.0, lo = 0.0;
         for (int64_t j = 0; j < K; ++j) {
             const double v = (double)load_elem(h, dtype, m * K + j);
-            ss += v * v;
+            dd_add(&hi, &lo, v * v);
         }
-        const float ms = (float)(ss / (double)K);
+        const float ms = (float)((hi + lo) / (double)K);
         const float r = 1.0f / sqrtf(ms + eps);
         for (int64_t j = 0; j < K; ++j) {
             const float v = load_elem(h, dtype, m * K + j);

@@ -282,3 +282,20 @@ def test_norm_quant_act_is_norm_then_per_row_quantize():
         for r in range(13):
             ref = int8_ref(y[r], sx[r]) if qt == "int8" else e4m3_ref(y[r], sx[r])
             np.testing.assert_array_equal(q[r], ref)
+
+
+def test_rms_norm_mean_is_order_free():
+    """The mean square is the (double-double) sum of exact squares: reversing the order of the
+    terms, or a row whose terms span 2^40 in magnitude, gives the float mean of math.fsum (the
+    correctly rounded sum).  Catches: a plain double sum, whose order shows in the last bits."""
+    import math
+    rng = np.random.Generator(np.random.PCG64(51))
+    h = rng.standard_normal((6, 4096)).astype(np.float32)
+    h *= np.exp2(rng.integers(-20, 20, h.shape)).astype(np.float32)
+    y = oracle.rms_norm(h, None, 0.0)
+    yr = oracle.rms_norm(h[:, ::-1].copy(), None, 0.0)[:, ::-1]
+    np.testing.assert_array_equal(y, yr)
+    for r in range(6):
+        ms = np.float32(math.fsum(float(v) * float(v) for v in h[r]) / 4096.0)
+        rr = np.float32(1.0) / np.sqrt(ms)
+        np.testing.assert_array_equal(y[r], (h[r] * rr).astype(np.float32))
