@@ -189,6 +189,27 @@ W8A8_API w8a8_status w8a8_gemm_dequant_tensor(const void* xq, const float* x_sca
                                       nullptr, stream));
 }
 
+// ---- RMS norm with the smoothing folded into its gain -------------------------------------------------
+
+W8A8_API w8a8_status w8a8_fold_norm_gain(const float* g, const float* s, int64_t K, float* g_out, hipStream_t stream) {
+    if (!g_out || K < 1 || K >= kMaxDim) return W8A8_ERR_INVALID_ARG;
+    return from_hip(w8a8::launch_fold_norm_gain(g, s, K, g_out, stream));
+}
+
+W8A8_API w8a8_status w8a8_norm_quant_act(const void* h, w8a8_dtype h_dtype, int64_t M, int64_t K, const float* g,
+                                         float eps, w8a8_qtype qtype, void* xq, float* x_scale, hipStream_t stream) {
+    if (!valid_dtype(h_dtype) || !valid_qtype(qtype)) return W8A8_ERR_INVALID_ARG;
+    if (!(eps >= 0.0f && eps < 1.0f)) return W8A8_ERR_INVALID_ARG;
+    if (M > 0 && (!h || !xq || !x_scale)) return W8A8_ERR_INVALID_ARG;
+    w8a8_status st = check_dims(M, 0, K);
+    if (st != W8A8_OK) return st;
+    if (K > 8192) return W8A8_ERR_UNSUPPORTED;            // rows are held in registers
+    if (M == 0) return W8A8_OK;
+    if (!aligned16(h) || !aligned16(g) || !aligned16(xq) || !aligned16(x_scale)) return W8A8_ERR_UNSUPPORTED;
+    return from_hip(w8a8::launch_norm_quant_act(h, h_dtype == W8A8_BF16, M, K, g, eps, qtype == W8A8_FP8_E4M3,
+                                                static_cast<uint8_t*>(xq), x_scale, stream));
+}
+
 // ---- weight-only W8A16 ------------------------------------------------------------------------------
 
 W8A8_API w8a8_status w8a8_gemm_w8a16(const void* x, const int8_t* wq, const float* w_scale, int64_t M, int64_t N,

@@ -354,6 +354,179 @@ __global__ __launch_bounds__(256) void quant_weight_t_kernel(const void* __restr
     }
 }
 
+// ---- RMS norm with the smoothing folded into its gain, then per-token quantize --------------------
+// ("Weight-Activation Quantization", s3 step 1: the SmoothQuant transform is done offline; the
+// W8A16-vs-W8A8 lesson, s2: no runtime overhead.)  X~[j] = (h[j] * r) * g'[j] with
+// g' = g / s folded once, r = 1 / sqrt(mean(h^2) + eps), then the per-token quantize of X~: one HBM
+// pass over the residual stream h, which replaces the norm kernel's output and the activation
+// quantize's read of it.
+//
+// The row is register-resident as in quant_act_kernel (kSplit waves per row).  The sum of squares
+// is carried in double-double (error-free TwoSum additions, then a butterfly across the wave and an
+// exchange across its parts), within about 2^-100 of the exact sum whatever the order, so the float
+// mean is the same as a sequential sum would give.
+
+// (hi, lo) + x for |lo| <= ulp(hi) / 2.
+__device__ __forceinline__ void dd_add(double& hi, double& lo, double x) {
+    const double s = hi + x;
+    const double bb = s - hi;
+    const double e = (hi - (s - bb)) + (x - bb) + lo;
+    hi = s + e;
+    lo = e - (hi - s);
+}
+
+// (hi, lo) + (h2, l2).
+__device__ __forceinline__ void dd_merge(double& hi, double& lo, double h2, double l2) {
+    const double s = hi + h2;
+    const double bb = s - hi;
+    const double e = (hi - (s - bb)) + (h2 - bb) + lo + l2;
+    hi = s + e;
+    lo = e - (hi - s);
+}
+
+template <bool kBf16, bool kFp8, int kChunks, bool kGain, int kSplit>
+__global__ __launch_bounds__(kActWaves * kWave) void norm_quant_kernel(
+    const void* __restrict__ h, const float* __restrict__ g, float eps, int64_t M, int64_t K, int rows_per_wave,
+    uint8_t* __restrict__ q, float* __restrict__ scale) {
+    extern __shared__ float sh_g[];             // kGain: g', K floats (lds_half order)
+    __shared__ double xhi[2][kActWaves], xlo[2][kActWaves];
+    __shared__ float xmax[2][kActWaves];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int64_t nchunk = K / 8;
+    if constexpr (kGain) {
+        constexpr int kPer = kSplit * kChunks;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int64_t j = threadIdx.x + static_cast<int64_t>(i) * blockDim.x;
+            if (j < K) sh_g[lds_half(j, nchunk)] = g[j];
+        }
+        __syncthreads();
+    }
+    constexpr int kRowsPerPass = kActWaves / kSplit;
+    const int slot = wave / kSplit;
+    const int part = wave % kSplit;
+    const int lane_c = part * kWave + lane;
+    constexpr int kStride = kSplit * kWave;
+    for (int rr = 0; rr < rows_per_wave; ++rr) {
+        const int64_t row = (static_cast<int64_t>(blockIdx.x) * rows_per_wave + rr) * kRowsPerPass + slot;
+        const bool live = row < M;
+        if (kSplit == 1 && !live) break;
+        const int64_t rrow = live ? row : M - 1;
+        Raw8<kBf16> raw[kChunks];
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) {
+            int64_t c = lane_c + static_cast<int64_t>(kStride) * i;
+            c = c < nchunk ? c : nchunk - 1;
+            raw[i] = load_raw8<kBf16>(h, rrow * K + c * 8);
+        }
+        float v[kChunks][8];
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) unpack8<kBf16>(raw[i], v[i]);
+        // Sum of squares over this lane's chunks (re-read chunks past the row end do not count).
+        double hi = 0.0, lo = 0.0;
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) {
+            if (lane_c + static_cast<int64_t>(kStride) * i < nchunk) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dd_add(hi, lo, static_cast<double>(v[i][e]) * static_cast<double>(v[i][e]));
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const double h2 = __shfl_xor(hi, off, kWave), l2 = __shfl_xor(lo, off, kWave);
+            dd_merge(hi, lo, h2, l2);
+        }
+        if constexpr (kSplit > 1) {
+            if (lane == 0) {
+                xhi[rr & 1][wave] = hi;
+                xlo[rr & 1][wave] = lo;
+            }
+            __syncthreads();
+            hi = xhi[rr & 1][slot * kSplit];
+            lo = xlo[rr & 1][slot * kSplit];
+#pragma unroll
+            for (int p = 1; p < kSplit; ++p) dd_merge(hi, lo, xhi[rr & 1][slot * kSplit + p], xlo[rr & 1][slot * kSplit + p]);
+        }
+        const float ms = static_cast<float>((hi + lo) / static_cast<double>(K));
+        const float r = div_rn(1.0f, __builtin_sqrtf(ms + eps));
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) {
+            int64_t c = lane_c + static_cast<int64_t>(kStride) * i;
+            c = c < nchunk ? c : nchunk - 1;
+            float gv[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
+            if constexpr (kGain) {
+                const float4 g0 = *reinterpret_cast<const float4*>(sh_g + c * 4);
+                const float4 g1 = *reinterpret_cast<const float4*>(sh_g + (nchunk + c) * 4);
+                gv[0] = g0.x; gv[1] = g0.y; gv[2] = g0.z; gv[3] = g0.w;
+                gv[4] = g1.x; gv[5] = g1.y; gv[6] = g1.z; gv[7] = g1.w;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                v[i][e] = (v[i][e] * r) * gv[e];
+                amax = fmaxf(amax, fabsf(v[i][e]));
+            }
+        }
+        amax = wave_max(amax);
+        if constexpr (kSplit > 1) {
+            if (lane == 0) xmax[rr & 1][wave] = amax;
+            __syncthreads();
+#pragma unroll
+            for (int p = 0; p < kSplit; ++p) amax = fmaxf(amax, xmax[rr & 1][slot * kSplit + p]);
+        }
+        if (!live) continue;
+        const float sc = div_rn(amax, qmax<kFp8>());
+        if (lane == 0 && part == 0) scale[row] = sc;
+        uint8_t* const qrow = q + row * K;
+        if (sc == 0.0f) {                       // a zero scale gives zero codes
+#pragma unroll
+            for (int i = 0; i < kChunks; ++i) {
+                const int64_t c = lane_c + static_cast<int64_t>(kStride) * i;
+                if (c < nchunk) *reinterpret_cast<uint2*>(qrow + c * 8) = make_uint2(0u, 0u);
+            }
+        } else if (in_pow2_range<-60, 60>(sc)) {
+            store_codes<kFp8, true>(v, sc, div_rn(1.0f, sc), lane_c, kStride, nchunk, qrow);
+        } else {
+            store_codes<kFp8, false>(v, sc, 0.0f, lane_c, kStride, nchunk, qrow);
+        }
+    }
+}
+
+template <bool kBf16, bool kFp8, int kChunks, int kSplit>
+void norm_quant_launch(const void* h, const float* g, float eps, int64_t M, int64_t K, uint8_t* xq, float* xs,
+                       hipStream_t st) {
+    const int64_t rows_per_pass = kActWaves / kSplit;
+    const int64_t rows_per_block_pass = rows_per_pass * 512;
+    const int rpw = static_cast<int>(std::max<int64_t>(1, (M + rows_per_block_pass - 1) / rows_per_block_pass));
+    const int64_t rows_per_block = rows_per_pass * rpw;
+    dim3 grid(static_cast<unsigned>((M + rows_per_block - 1) / rows_per_block)), block(kActWaves * kWave);
+    if (g)
+        hipLaunchKernelGGL((norm_quant_kernel<kBf16, kFp8, kChunks, true, kSplit>), grid, block,
+                           static_cast<size_t>(K) * sizeof(float), st, h, g, eps, M, K, rpw, xq, xs);
+    else
+        hipLaunchKernelGGL((norm_quant_kernel<kBf16, kFp8, kChunks, false, kSplit>), grid, block, 0, st, h, g, eps, M,
+                           K, rpw, xq, xs);
+}
+
+template <bool kBf16, bool kFp8>
+hipError_t norm_quant_dispatch(const void* h, const float* g, float eps, int64_t M, int64_t K, uint8_t* xq, float* xs,
+                               hipStream_t st) {
+    const int64_t per_lane = (K / 8 + kWave - 1) / kWave;
+    if (per_lane <= 1) norm_quant_launch<kBf16, kFp8, 1, 1>(h, g, eps, M, K, xq, xs, st);
+    else if (per_lane <= 2) norm_quant_launch<kBf16, kFp8, 2, 1>(h, g, eps, M, K, xq, xs, st);
+    else if (per_lane <= 4) norm_quant_launch<kBf16, kFp8, 4, 1>(h, g, eps, M, K, xq, xs, st);
+    else if (per_lane <= 8) norm_quant_launch<kBf16, kFp8, 4, 2>(h, g, eps, M, K, xq, xs, st);
+    else if (per_lane <= 16) norm_quant_launch<kBf16, kFp8, 4, 4>(h, g, eps, M, K, xq, xs, st);
+    else return hipErrorInvalidValue;       // K > 8192: refused by the C ABI before this point
+    return hipGetLastError();
+}
+
+__global__ void fold_gain_kernel(const float* __restrict__ g, const float* __restrict__ s, int64_t K,
+                                 float* __restrict__ out) {
+    const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (j < K) out[j] = div_rn(g ? g[j] : 1.0f, s ? s[j] : 1.0f);
+}
+
 template <bool kBf16, bool kFp8, int kChunks, int kSplit>
 void quant_act_launch(const void* x, int64_t M, int64_t K, const float* s, uint8_t* xq, float* xs, hipStream_t st) {
     // Rows per wave: one, or more once there are enough rows for two blocks per CU on 256 CUs.
@@ -491,6 +664,21 @@ hipError_t launch_quant_act(const void* x, bool bf16, int64_t M, int64_t K, cons
                          : quant_act_dispatch<true, false>(x, M, K, s, xq, x_scale, st);
     return fp8 ? quant_act_dispatch<false, true>(x, M, K, s, xq, x_scale, st)
                : quant_act_dispatch<false, false>(x, M, K, s, xq, x_scale, st);
+}
+
+hipError_t launch_norm_quant_act(const void* h, bool bf16, int64_t M, int64_t K, const float* g, float eps, bool fp8,
+                                 uint8_t* xq, float* x_scale, hipStream_t st) {
+    if (M <= 0) return hipSuccess;
+    if (bf16) return fp8 ? norm_quant_dispatch<true, true>(h, g, eps, M, K, xq, x_scale, st)
+                         : norm_quant_dispatch<true, false>(h, g, eps, M, K, xq, x_scale, st);
+    return fp8 ? norm_quant_dispatch<false, true>(h, g, eps, M, K, xq, x_scale, st)
+               : norm_quant_dispatch<false, false>(h, g, eps, M, K, xq, x_scale, st);
+}
+
+hipError_t launch_fold_norm_gain(const float* g, const float* s, int64_t K, float* out, hipStream_t st) {
+    if (K <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fold_gain_kernel, dim3(static_cast<unsigned>((K + 255) / 256)), dim3(256), 0, st, g, s, K, out);
+    return hipGetLastError();
 }
 
 hipError_t launch_quant_weight_t(const void* w, bool bf16, int64_t K, int64_t N, const float* s,

@@ -175,6 +175,28 @@ w8a8_status w8a8_gemm_dequant_tensor(const void* xq, const float* x_scale, const
                                      int64_t K, void* y, hipStream_t stream);
 
 /*
+ * ---- The smoothing folded into the layer before ([WAQ] s3 step 1: the SmoothQuant transform is
+ * done offline, during model preparation; the W8A16-vs-W8A8 lesson, s2: no runtime overhead).
+ * The activations X come from an RMS norm of the residual stream h with gain g; 1/s is folded into
+ * that gain once, and the norm, the smoothing and the per-token quantize run as one pass over h.
+ */
+
+/* g_out[j] = g[j] / s[j] (fp32, correctly rounded); g or s NULL count as 1.  K >= 1. */
+w8a8_status w8a8_fold_norm_gain(const float* g, const float* s, int64_t K, float* g_out, hipStream_t stream);
+
+/*
+ * Per row i of h [M, K] (h_dtype):
+ *   ms       = (float)(sum_j (double)h[i, j]^2 / K)   (the sum exact to about 2^-100: order-free)
+ *   r        = 1 / sqrt(ms + eps)                     (fp32, correctly rounded root and division)
+ *   X~[i, j] = (h[i, j] * r) * g[j]                   (fp32, in this order; g NULL: 1)
+ * then x_scale[i] and xq[i, :] exactly as w8a8_quant_act gives for X~ with s == NULL.
+ * g: fp32 [K], normally the output of w8a8_fold_norm_gain.  eps in [0, 1).  K <= 8192 (rows are
+ * held in registers), else W8A8_ERR_UNSUPPORTED.  xq: [M, K] bytes, x_scale: fp32 [M].
+ */
+w8a8_status w8a8_norm_quant_act(const void* h, w8a8_dtype h_dtype, int64_t M, int64_t K, const float* g,
+                                float eps, w8a8_qtype qtype, void* xq, float* x_scale, hipStream_t stream);
+
+/*
  * ---- Weight-only W8A16, the contrast the pages draw with W8A8 ([WAQ] s1 "Why Quantize Activations
  * Too?": weight-only quantization keeps the GEMM in 16-bit; the W8A16-vs-W8A8 lesson, s1: the 8-bit
  * weights are dequantized to 16-bit on the fly and the multiply runs on 16-bit tensor cores).

@@ -1,0 +1,101 @@
+"""Parity of the fused RMS norm + per-token quantize (the smoothing folded into the norm's gain:
+"Weight-Activation Quantization", s3 step 1 done offline; the W8A16-vs-W8A8 lesson, s2) with the
+CPU oracle, through the C ABI.
+
+Bar: the folded gain, the scales and the codes bit-exact (INT8 and E4M3), f32 and bf16 inputs,
+row lengths for every register layout (one wave per row up to four), ragged rows and row counts,
+rows with outliers and rows spanning 2^40 in magnitude, zero rows, and the prefill shape.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import announce, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def f():
+    import fp8_gemm_amd
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    fp8_gemm_amd.w8a8_version()
+    assert fp8_gemm_amd.lib_path() in open("/proc/self/maps").read(), "libw8a8.so is not loaded"
+    return fp8_gemm_amd
+
+
+def codes(a):
+    return np.ascontiguousarray(a).view(np.uint8)
+
+
+def folded_gain(f, K, seed):
+    g = synth.random_scales(K, seed=seed, lo=0.5, hi=2.0)
+    s = synth.random_scales(K, seed=seed + 1, lo=0.05, hi=20.0)
+    gf = f.w8a8_fold_norm_gain(dev(g), dev(s))
+    torch.cuda.synchronize()
+    gf = host(gf)
+    np.testing.assert_array_equal(gf, oracle.fold_norm_gain(g, s))
+    return gf
+
+
+# (M, K): one wave per row (K <= 512, 1024, 2048), two (<= 4096), four (<= 8192); ragged tails
+SHAPES = [(1, 16), (5, 48), (33, 512), (70, 1040), (129, 2064), (64, 4096), (19, 6160), (40, 8192)]
+
+
+@pytest.mark.parametrize("qtype", ["int8", "fp8"])
+@pytest.mark.parametrize("M,K", SHAPES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_norm_quant_act(f, qtype, M, K, dtype):
+    announce(f"norm_quant_act {qtype} {dtype} {M}x{K}")
+    H = synth.random_matrix((M, K), seed=M * 13 + K, dtype=dtype, outliers=max(1, K // 100))
+    gf = folded_gain(f, K, seed=K)
+    for g, eps in ((gf, 1e-5), (None, 1e-6)):
+        xq, sx = f.w8a8_norm_quant_act(dev(H), None if g is None else dev(g), eps, qtype)
+        torch.cuda.synchronize()
+        q_ref, sx_ref = oracle.norm_quant_act(H, g, eps, qtype)
+        np.testing.assert_array_equal(host(sx), sx_ref)
+        np.testing.assert_array_equal(codes(host(xq)), codes(q_ref))
+
+
+@pytest.mark.parametrize("qtype", ["int8", "fp8"])
+def test_norm_quant_act_wide_range_and_zero_rows(f, qtype):
+    """Rows whose squares span 2^80 (the double-double sum must match the oracle's), an all-zero row
+    (scale 0, codes 0), and eps = 0."""
+    announce(f"norm_quant_act wide range {qtype}")
+    rng = np.random.Generator(np.random.PCG64(77))
+    H = rng.standard_normal((48, 4096)).astype(np.float32)
+    H *= np.exp2(rng.integers(-20, 20, H.shape)).astype(np.float32)
+    H[5] = 0.0
+    gf = folded_gain(f, 4096, seed=78)
+    xq, sx = f.w8a8_norm_quant_act(dev(H), dev(gf), 1e-5, qtype)
+    torch.cuda.synchronize()
+    q_ref, sx_ref = oracle.norm_quant_act(H, gf, 1e-5, qtype)
+    np.testing.assert_array_equal(host(sx), sx_ref)
+    np.testing.assert_array_equal(codes(host(xq)), codes(q_ref))
+    assert sx_ref[5] == 0 and np.all(q_ref[5] == 0)
+    Hn = np.delete(H, 5, axis=0)
+    xq, sx = f.w8a8_norm_quant_act(dev(Hn), dev(gf), 0.0, qtype)
+    torch.cuda.synchronize()
+    q_ref, sx_ref = oracle.norm_quant_act(Hn, gf, 0.0, qtype)
+    np.testing.assert_array_equal(host(sx), sx_ref)
+    np.testing.assert_array_equal(codes(host(xq)), codes(q_ref))
+
+
+def test_norm_quant_act_prefill_shape(f):
+    """The prefill workload's activations as the residual stream (2048 x 4096, bf16, outlier
+    channels), the smoothing factors of that workload folded into a random gain."""
+    announce("norm_quant_act prefill shape")
+    X, W = synth.make_inputs("c2")
+    x, w = dev(X), dev(W)
+    _, _, s = f.w8a8_smooth_scales(x, w, 0.5)
+    g = synth.random_scales(X.shape[1], seed=79, lo=0.5, hi=2.0)
+    gf = f.w8a8_fold_norm_gain(dev(g), s)
+    xq, sx = f.w8a8_norm_quant_act(x, gf, 1e-5, "int8")
+    torch.cuda.synchronize()
+    gf_h = host(gf)
+    np.testing.assert_array_equal(gf_h, oracle.fold_norm_gain(g, host(s)))
+    q_ref, sx_ref = oracle.norm_quant_act(X, gf_h, 1e-5, "int8")
+    np.testing.assert_array_equal(host(sx), sx_ref)
+    np.testing.assert_array_equal(host(xq), q_ref)
