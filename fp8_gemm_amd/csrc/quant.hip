@@ -361,10 +361,14 @@ __global__ __launch_bounds__(256) void quant_weight_t_kernel(const void* __restr
 // pass over the residual stream h, which replaces the norm kernel's output and the activation
 // quantize's read of it.
 //
-// The row is register-resident as in quant_act_kernel (kSplit waves per row).  The sum of squares
-// is carried in double-double (error-free TwoSum additions, then a butterfly across the wave and an
-// exchange across its parts), within about 2^-100 of the exact sum whatever the order, so the float
-// mean is the same as a sequential sum would give.
+// The row is register-resident as in quant_act_kernel (kSplit waves per row).  The float mean
+// square must not depend on the order of the sum.  Each square of a float is exact in double, and a
+// plain double sum of them through at most 41 additions (32 per lane, 6 across the wave, 3 across
+// the parts) is within 41 * 2^-53 < 2^-47 of the exact sum.  The mean is taken as certified when
+// both ends of a 2^-44 band around the estimate round to the same float: the exactly rounded mean
+// lies in the band, so it is that float.  Otherwise (about one row in 2^19) the sum is redone in
+// double-double (error-free TwoSum additions, within about 2^-100 of the exact sum in any order)
+// and the mean taken from it, as a sequential exact sum would give it.
 
 // (hi, lo) + x for |lo| <= ulp(hi) / 2.
 __device__ __forceinline__ void dd_add(double& hi, double& lo, double x) {
@@ -384,12 +388,55 @@ __device__ __forceinline__ void dd_merge(double& hi, double& lo, double h2, doub
     lo = e - (hi - s);
 }
 
+// The float mean of a sum estimate within 2^-47 of the exact sum, or -1 when the band around it
+// straddles a float rounding boundary.  inv_k = 1/K in double (relative error 2^-53).
+__device__ __forceinline__ float certified_mean(double sum, double inv_k) {
+    const double q = sum * inv_k;
+    const float lo = static_cast<float>(q - q * 0x1p-44);
+    const float hi = static_cast<float>(q + q * 0x1p-44);
+    return lo == hi ? lo : -1.0f;
+}
+
+// The row's mean square from the double-double sum of this lane's squares: a butterfly across the
+// wave, then (kSplit > 1) an exchange across the row's waves.  Called by every wave of the block.
+template <int kChunks, int kSplit>
+__device__ __forceinline__ float dd_mean(const float (&v)[kChunks][8], int lane_c, int64_t nchunk, int64_t K,
+                                         int lane, int wave, int slot, double (*xhi)[kActWaves],
+                                         double (*xlo)[kActWaves], int buf) {
+    constexpr int kStride = kSplit * kWave;
+    double hi = 0.0, lo = 0.0;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+        if (lane_c + static_cast<int64_t>(kStride) * i < nchunk) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dd_add(hi, lo, static_cast<double>(v[i][e]) * static_cast<double>(v[i][e]));
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const double h2 = __shfl_xor(hi, off, kWave), l2 = __shfl_xor(lo, off, kWave);
+        dd_merge(hi, lo, h2, l2);
+    }
+    if constexpr (kSplit > 1) {
+        if (lane == 0) {
+            xhi[buf][wave] = hi;
+            xlo[buf][wave] = lo;
+        }
+        __syncthreads();
+        hi = xhi[buf][slot * kSplit];
+        lo = xlo[buf][slot * kSplit];
+#pragma unroll
+        for (int p = 1; p < kSplit; ++p) dd_merge(hi, lo, xhi[buf][slot * kSplit + p], xlo[buf][slot * kSplit + p]);
+    }
+    return static_cast<float>((hi + lo) / static_cast<double>(K));
+}
+
 template <bool kBf16, bool kFp8, int kChunks, bool kGain, int kSplit>
 __global__ __launch_bounds__(kActWaves * kWave) void norm_quant_kernel(
     const void* __restrict__ h, const float* __restrict__ g, float eps, int64_t M, int64_t K, int rows_per_wave,
     uint8_t* __restrict__ q, float* __restrict__ scale) {
     extern __shared__ float sh_g[];             // kGain: g', K floats (lds_half order)
-    __shared__ double xhi[2][kActWaves], xlo[2][kActWaves];
+    __shared__ double xsum[2][kActWaves], xhi[2][kActWaves], xlo[2][kActWaves];
     __shared__ float xmax[2][kActWaves];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int64_t nchunk = K / 8;
@@ -422,32 +469,44 @@ __global__ __launch_bounds__(kActWaves * kWave) void norm_quant_kernel(
         float v[kChunks][8];
 #pragma unroll
         for (int i = 0; i < kChunks; ++i) unpack8<kBf16>(raw[i], v[i]);
-        // Sum of squares over this lane's chunks (re-read chunks past the row end do not count).
-        double hi = 0.0, lo = 0.0;
+        // Sum of squares over this lane's chunks (re-read chunks past the row end do not count): a
+        // plain double sum of exact squares, the same in every lane after the xor butterfly.
+        double sum = 0.0;
 #pragma unroll
         for (int i = 0; i < kChunks; ++i) {
             if (lane_c + static_cast<int64_t>(kStride) * i < nchunk) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) dd_add(hi, lo, static_cast<double>(v[i][e]) * static_cast<double>(v[i][e]));
+                for (int e = 0; e < 8; ++e) {
+                    const double d = static_cast<double>(v[i][e]);
+                    sum = __builtin_fma(d, d, sum);
+                }
             }
         }
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const double h2 = __shfl_xor(hi, off, kWave), l2 = __shfl_xor(lo, off, kWave);
-            dd_merge(hi, lo, h2, l2);
-        }
-        if constexpr (kSplit > 1) {
-            if (lane == 0) {
-                xhi[rr & 1][wave] = hi;
-                xlo[rr & 1][wave] = lo;
-            }
+        for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, kWave);
+        const double inv_k = 1.0 / static_cast<double>(K);
+        float ms;
+        if constexpr (kSplit == 1) {
+            ms = certified_mean(sum, inv_k);
+            if (ms < 0.0f) ms = dd_mean<kChunks, 1>(v, lane_c, nchunk, K, lane, wave, slot, xhi, xlo, rr & 1);
+        } else {
+            // Every wave certifies every row of the pass, so the fallback (which has a barrier) is
+            // taken by the whole block or not at all.
+            if (lane == 0) xsum[rr & 1][wave] = sum;
             __syncthreads();
-            hi = xhi[rr & 1][slot * kSplit];
-            lo = xlo[rr & 1][slot * kSplit];
+            bool straddle = false;
+            ms = 0.0f;
 #pragma unroll
-            for (int p = 1; p < kSplit; ++p) dd_merge(hi, lo, xhi[rr & 1][slot * kSplit + p], xlo[rr & 1][slot * kSplit + p]);
+            for (int t = 0; t < kRowsPerPass; ++t) {
+                double st = xsum[rr & 1][t * kSplit];
+#pragma unroll
+                for (int p = 1; p < kSplit; ++p) st += xsum[rr & 1][t * kSplit + p];
+                const float mt = certified_mean(st, inv_k);
+                straddle |= mt < 0.0f;
+                if (t == slot) ms = mt;
+            }
+            if (straddle) ms = dd_mean<kChunks, kSplit>(v, lane_c, nchunk, K, lane, wave, slot, xhi, xlo, rr & 1);
         }
-        const float ms = static_cast<float>((hi + lo) / static_cast<double>(K));
         const float r = div_rn(1.0f, __builtin_sqrtf(ms + eps));
         float amax = 0.0f;
 #pragma unroll

@@ -145,3 +145,26 @@ def random_codes(shape, seed: int, qtype: str = INT8) -> np.ndarray:
 def random_scales(n: int, seed: int, lo: float = 1e-3, hi: float = 1e-1) -> np.ndarray:
     rng = np.random.Generator(np.random.PCG64(seed))
     return rng.uniform(lo, hi, n).astype(np.float32)
+
+
+def mean_square_tie_rows(K: int) -> np.ndarray:
+    """Two float32 rows of length K (a power of two, >= 16) built from powers of two.
+
+    Row 0: one 8.0 (two when log2(K) is even), then the rest of a sum of squares that puts the mean
+    square exactly halfway between two adjacent floats.  Row 1: the same plus six squares of 2^-24
+    placed after the 8.0 in its first 8 elements, each below half an ulp of the running sum there,
+    so that a sequential double sum drops them while the exact mean lies just past the halfway
+    point.  The odd power of two keeps the square root of the mean inexact, so a one-ulp change in
+    the mean shows in the normalized row."""
+    assert K >= 16 and K & (K - 1) == 0
+    two = (K.bit_length() - 1) % 2 == 0
+    rows = np.zeros((2, K), np.float32)
+    rows[:, 0] = 8.0
+    if two:
+        rows[:, 2] = 8.0
+        rows[:, 8:10] = 2.0 ** -9           # 2 * 2^-18 = half an ulp of 128 / K, times K
+    else:
+        rows[:, 8] = 2.0 ** -9              # 2^-18 = half an ulp of 64 / K, times K
+    small = [1, 3, 4, 5, 6, 7]
+    rows[1, small] = 2.0 ** -24
+    return rows

@@ -83,6 +83,32 @@ def test_norm_quant_act_wide_range_and_zero_rows(f, qtype):
     np.testing.assert_array_equal(codes(host(xq)), codes(q_ref))
 
 
+@pytest.mark.parametrize("qtype", ["int8", "fp8"])
+@pytest.mark.parametrize("K", [128, 1024, 2048, 4096, 8192])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_norm_quant_act_mean_square_tie(f, qtype, K, dtype):
+    """Rows whose mean square sits on a float rounding tie, or just past it by squares that a plain
+    double sum drops (the rows normalize differently, so a mean taken from such a sum fails), among
+    random rows: in the first and last pass of a block, and alone or in pairs within one pass."""
+    announce(f"norm_quant_act mean square tie {qtype} {dtype} K={K}")
+    M = 37
+    H = synth.random_matrix((M, K), seed=K + 5, outliers=max(1, K // 100))
+    tie = synth.mean_square_tie_rows(K)
+    for r0 in (0, 6, 17, 35):
+        H[r0:r0 + 2] = tie
+    if dtype == "bf16":
+        H = synth.f32_to_bf16_bits(H)
+    gf = folded_gain(f, K, seed=K + 6)
+    for g, eps in ((None, 0.0), (gf, 0.0), (gf, 1e-5)):
+        xq, sx = f.w8a8_norm_quant_act(dev(H), None if g is None else dev(g), eps, qtype)
+        torch.cuda.synchronize()
+        q_ref, sx_ref = oracle.norm_quant_act(H, g, eps, qtype)
+        np.testing.assert_array_equal(host(sx), sx_ref)
+        np.testing.assert_array_equal(codes(host(xq)), codes(q_ref))
+        if g is None:
+            assert sx_ref[0] != sx_ref[1]
+
+
 def test_norm_quant_act_prefill_shape(f):
     """The prefill workload's activations as the residual stream (2048 x 4096, bf16, outlier
     channels), the smoothing factors of that workload folded into a random gain."""

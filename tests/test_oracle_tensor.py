@@ -11,6 +11,7 @@ import json
 import os
 
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -299,3 +300,23 @@ def test_rms_norm_mean_is_order_free():
         ms = np.float32(math.fsum(float(v) * float(v) for v in h[r]) / 4096.0)
         rr = np.float32(1.0) / np.sqrt(ms)
         np.testing.assert_array_equal(y[r], (h[r] * rr).astype(np.float32))
+
+
+@pytest.mark.parametrize("K", [16, 128, 1024, 4096, 8192])
+def test_rms_norm_mean_square_tie(K):
+    """Rows whose mean square is exactly halfway between two floats (rounds to even), and the same
+    just past halfway through squares that a sequential double sum drops: the oracle's mean is the
+    correctly rounded one (math.fsum of the exact squares over K, a power of two) in both, and the
+    two rows normalize differently.  Catches: a plain double sum, a mean rounded twice."""
+    import math
+    h = synth.mean_square_tie_rows(K)
+    y = oracle.rms_norm(h, None, 0.0)
+    seq = 0.0
+    for v in h[1].astype(np.float64):
+        seq += v * v
+    for r in range(2):
+        ms = np.float32(math.fsum(float(v) * float(v) for v in h[r]) / K)
+        rr = np.float32(1.0) / np.sqrt(ms)
+        np.testing.assert_array_equal(y[r], (h[r] * rr).astype(np.float32))
+    assert np.float32(seq / K) == np.float32(math.fsum(float(v) * float(v) for v in h[0]) / K)
+    assert y[0, 0] != y[1, 0]
