@@ -24,7 +24,8 @@ W8A8_OK, W8A8_ERR_INVALID_ARG, W8A8_ERR_UNSUPPORTED, W8A8_ERR_HIP = 0, 1, 2, 3
 W8A8_F32, W8A8_BF16 = 0, 1
 W8A8_INT8, W8A8_FP8_E4M3 = 0, 1
 
-ENTRY_POINTS = ("w8a8_smooth_scales", "w8a8_fold_quant_weight", "w8a8_quant_act", "w8a8_gemm_dequant",
+ENTRY_POINTS = ("w8a8_smooth_scales", "w8a8_fold_quant_weight", "w8a8_quant_act", "w8a8_smooth_quant",
+                "w8a8_gemm_dequant",
                 "w8a8_gemm_i32", "w8a8_gemm_f32", "w8a8_absmax", "w8a8_quant_act_tensor",
                 "w8a8_quant_weight_tensor", "w8a8_gemm_dequant_tensor", "w8a8_gemm_w8a16", "w8a8_fold_norm_gain",
                 "w8a8_norm_quant_act", "w8a8_status_string", "w8a8_version")
@@ -51,6 +52,7 @@ def _load() -> ctypes.CDLL:
         "w8a8_smooth_scales": (I, [P, I, I64, I64, P, I, I64, F, P, P, I, P, P]),
         "w8a8_fold_quant_weight": (I, [P, I, I64, I64, P, I, P, P, P]),
         "w8a8_quant_act": (I, [P, I, I64, I64, P, I, P, P, P]),
+        "w8a8_smooth_quant": (I, [P, I, I64, I64, P, I, I64, F, I, P, P, P, P, P, P, P, P]),
         "w8a8_gemm_dequant": (I, [P, P, P, P, I, I64, I64, I64, P, P]),
         "w8a8_gemm_i32": (I, [P, P, I64, I64, I64, P, P]),
         "w8a8_gemm_f32": (I, [P, P, I64, I64, I64, P, P]),
@@ -169,6 +171,31 @@ def w8a8_quant_act(x, s=None, qtype="int8", xq=None, x_scale=None, stream=None):
     return xq, x_scale
 
 
+def w8a8_smooth_quant(x, w, alpha: float = 0.5, qtype="int8", out=None, stream=None):
+    """Calibration, smoothing factors, weight fold + quantize and activation quantize in one call.
+    Returns a dict ax, aw, s [K], wq [N, K], w_scale [N], xq [M, K], x_scale [M] (``out``: a dict
+    of such tensors to write into)."""
+    _dev(x, "x"), _dev(w, "w")
+    q = _qtype(qtype)
+    M, K = x.shape
+    K2, N = w.shape
+    if K2 != K:
+        raise ValueError("x is [M, K] and w is [K, N]")
+    dev = x.device
+    if out is None:
+        f32 = dict(dtype=torch.float32, device=dev)
+        out = dict(ax=torch.empty(K, **f32), aw=torch.empty(K, **f32), s=torch.empty(K, **f32),
+                   wq=torch.empty((N, K), dtype=_code_dtype(q), device=dev), w_scale=torch.empty(N, **f32),
+                   xq=torch.empty((M, K), dtype=_code_dtype(q), device=dev), x_scale=torch.empty(M, **f32))
+    for name in ("ax", "aw", "s", "wq", "w_scale", "xq", "x_scale"):
+        _dev(out[name], name)
+    _check("w8a8_smooth_quant", _load().w8a8_smooth_quant(
+        _ptr(x), _dtype(x), M, K, _ptr(w), _dtype(w), N, float(alpha), q, _ptr(out["ax"]), _ptr(out["aw"]),
+        _ptr(out["s"]), _ptr(out["wq"]), _ptr(out["w_scale"]), _ptr(out["xq"]), _ptr(out["x_scale"]),
+        _stream(stream)))
+    return out
+
+
 def w8a8_gemm_dequant(xq, x_scale, wq, w_scale, qtype="int8", y=None, stream=None):
     """Quantized GEMM + dequantize: returns Y bfloat16 [M, N]."""
     for t, n in ((xq, "xq"), (x_scale, "x_scale"), (wq, "wq"), (w_scale, "w_scale")):
@@ -208,14 +235,19 @@ def w8a8_gemm_f32(xq, wq, acc=None, stream=None):
     return acc
 
 
-def w8a8_layer(x, w, alpha: float = 0.5, qtype="int8", stream=None):
-    """The whole path for one batch that is also its own calibration set:
-    smooth_scales -> fold_quant_weight -> quant_act -> gemm_dequant.  Returns a dict of tensors."""
-    ax, aw, s = w8a8_smooth_scales(x, w, alpha, stream=stream)
-    wq, w_scale = w8a8_fold_quant_weight(w, s, qtype, stream=stream)
-    xq, x_scale = w8a8_quant_act(x, s, qtype, stream=stream)
-    y = w8a8_gemm_dequant(xq, x_scale, wq, w_scale, qtype, stream=stream)
-    return dict(ax=ax, aw=aw, s=s, wq=wq, w_scale=w_scale, xq=xq, x_scale=x_scale, y=y)
+def w8a8_layer(x, w, alpha: float = 0.5, qtype="int8", fused: bool = True, stream=None):
+    """The whole path for one batch that is also its own calibration set: smooth_quant (or, with
+    fused=False, smooth_scales -> fold_quant_weight -> quant_act) -> gemm_dequant.  Returns a dict
+    of tensors."""
+    if fused:
+        r = w8a8_smooth_quant(x, w, alpha, qtype, stream=stream)
+    else:
+        ax, aw, s = w8a8_smooth_scales(x, w, alpha, stream=stream)
+        wq, w_scale = w8a8_fold_quant_weight(w, s, qtype, stream=stream)
+        xq, x_scale = w8a8_quant_act(x, s, qtype, stream=stream)
+        r = dict(ax=ax, aw=aw, s=s, wq=wq, w_scale=w_scale, xq=xq, x_scale=x_scale)
+    r["y"] = w8a8_gemm_dequant(r["xq"], r["x_scale"], r["wq"], r["w_scale"], qtype, stream=stream)
+    return r
 
 
 # ---- per-tensor scaling (one scale per tensor, held in a 1-element float32 tensor) ----------------

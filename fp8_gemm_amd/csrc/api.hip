@@ -74,6 +74,40 @@ W8A8_API w8a8_status w8a8_fold_quant_weight(const void* w, w8a8_dtype w_dtype, i
     return from_hip(e);
 }
 
+W8A8_API w8a8_status w8a8_smooth_quant(const void* x, w8a8_dtype x_dtype, int64_t M, int64_t K, const void* w,
+                                       w8a8_dtype w_dtype, int64_t N, float alpha, w8a8_qtype qtype, float* ax,
+                                       float* aw, float* s, void* wq, float* w_scale, void* xq, float* x_scale,
+                                       hipStream_t stream) {
+    if (!valid_dtype(x_dtype) || !valid_dtype(w_dtype) || !valid_qtype(qtype)) return W8A8_ERR_INVALID_ARG;
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return W8A8_ERR_INVALID_ARG;
+    if (!ax || !aw || !s) return W8A8_ERR_INVALID_ARG;
+    if (M > 0 && (!x || !xq || !x_scale)) return W8A8_ERR_INVALID_ARG;
+    if (N > 0 && (!w || !wq || !w_scale)) return W8A8_ERR_INVALID_ARG;
+    w8a8_status st = check_dims(M, N, K);
+    if (st != W8A8_OK) return st;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(ax) || !aligned16(aw) || !aligned16(s) || !aligned16(wq) ||
+        !aligned16(w_scale) || !aligned16(xq) || !aligned16(x_scale))
+        return W8A8_ERR_UNSUPPORTED;
+    const bool fp8 = qtype == W8A8_FP8_E4M3;
+    const bool fused = x_dtype == w_dtype && M >= 1 && N >= 1 && N % 8 == 0 && K <= 8192 && M < (int64_t(1) << 23) &&
+                       N < (int64_t(1) << 23);
+    if (!fused) {
+        st = w8a8_smooth_scales(x, x_dtype, M, K, w, w_dtype, N, alpha, ax, aw, 0, s, stream);
+        if (st == W8A8_OK) st = w8a8_fold_quant_weight(w, w_dtype, K, N, s, qtype, wq, w_scale, stream);
+        if (st == W8A8_OK) st = w8a8_quant_act(x, x_dtype, M, K, s, qtype, xq, x_scale, stream);
+        return st;
+    }
+    const bool bf16 = x_dtype == W8A8_BF16;
+    hipError_t e = w8a8::launch_zero2(ax, K, w_scale, N, stream);
+    if (e == hipSuccess) e = w8a8::launch_calib_pair(x, w, bf16, M, K, N, ax, aw, stream);
+    if (e == hipSuccess)
+        e = w8a8::launch_fold_cols(w, bf16, K, N, ax, aw, alpha, fp8 ? 448.0f : 127.0f, s, w_scale, stream);
+    if (e == hipSuccess)
+        e = w8a8::launch_quant_pair(x, bf16, M, K, s, fp8, static_cast<uint8_t*>(xq), x_scale, w, N, w_scale,
+                                    static_cast<uint8_t*>(wq), stream);
+    return from_hip(e);
+}
+
 W8A8_API w8a8_status w8a8_quant_act(const void* x, w8a8_dtype x_dtype, int64_t M, int64_t K, const float* s,
                                     w8a8_qtype qtype, void* xq, float* x_scale, hipStream_t stream) {
     if (!valid_dtype(x_dtype) || !valid_qtype(qtype)) return W8A8_ERR_INVALID_ARG;

@@ -21,6 +21,13 @@ __global__ void fill_kernel(float* p, int64_t n, float v) {
     if (i < n) p[i] = v;
 }
 
+// Zeroes p[0, n) and q[0, m) in one launch.
+__global__ void zero2_kernel(float* p, int64_t n, float* q, int64_t m) {
+    int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+    else if (i - n < m) q[i - n] = 0.0f;
+}
+
 template <bool kBf16>
 __device__ __forceinline__ float load1(const void* base, int64_t i) {
     if constexpr (kBf16) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(base)[i]) << 16);
@@ -47,15 +54,18 @@ __device__ __forceinline__ void load_chunk(const void* base, int64_t row_start, 
 // R - 1 and columns past C re-read the last chunk: duplicates do not change a maximum.  With
 // divisor != 0 the block maxima are divided by it before they are merged: correctly rounded
 // division is monotone, so the merged value is the maximum divided by divisor, rounded once.
-template <bool kBf16, bool kVec, bool kScaled>
-__global__ __launch_bounds__(256) void absmax_cols_kernel(const void* __restrict__ a, int64_t R, int64_t C,
-                                                          const float* __restrict__ row_scale, float divisor,
-                                                          float* __restrict__ out) {
-    __shared__ float part[4][kColsPerWave];
+//
+// The body serves a block of 4 waves (bx, by) = (column block, row block); row_scale[i] is the
+// factor of row r0 + i of the block (rows past R use that of row R - 1).  pre() runs once the
+// block's loads are in flight and before the factors are read (the fold computes them there).
+template <bool kBf16, bool kVec, bool kScaled, typename Pre>
+__device__ __forceinline__ void cols_body(const void* __restrict__ a, int64_t R, int64_t C,
+                                          const float* row_scale, float divisor, float* __restrict__ out,
+                                          int64_t bx, int64_t by, float (*part)[kColsPerWave], Pre pre) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int64_t c = static_cast<int64_t>(blockIdx.x) * kColsPerWave + lane * 8;
+    const int64_t c = bx * kColsPerWave + lane * 8;
     const int64_t cl = c < C ? c : (kVec ? C - 8 : C - 1);
-    const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kRowsPerBlock;
+    const int64_t r0 = by * kRowsPerBlock;
     constexpr int kRows = kRowsPerBlock / 4;
     float v[kRows][8];
 #pragma unroll
@@ -64,13 +74,14 @@ __global__ __launch_bounds__(256) void absmax_cols_kernel(const void* __restrict
         r = r < R ? r : R - 1;
         load_chunk<kBf16, kVec>(a, r * C, cl, C, v[i]);
     }
+    pre();
     float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
         float rs = 1.0f;
         if constexpr (kScaled) {
             const int64_t r = r0 + wave + 4 * i;
-            rs = row_scale[r < R ? r : R - 1];
+            rs = row_scale[(r < R ? r : R - 1) - r0];
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) m[e] = fmaxf(m[e], fabsf(kScaled ? rs * v[i][e] : v[i][e]));
@@ -78,14 +89,28 @@ __global__ __launch_bounds__(256) void absmax_cols_kernel(const void* __restrict
 #pragma unroll
     for (int e = 0; e < 8; ++e) part[wave][lane * 8 + e] = m[e];
     __syncthreads();
-    for (int i = threadIdx.x; i < kColsPerWave; i += blockDim.x) {
-        const int64_t col = static_cast<int64_t>(blockIdx.x) * kColsPerWave + i;
+    for (int i = threadIdx.x; i < kColsPerWave; i += 4 * kWave) {
+        const int64_t col = bx * kColsPerWave + i;
         if (col < C) {
             float mv = fmaxf(fmaxf(part[0][i], part[1][i]), fmaxf(part[2][i], part[3][i]));
             if (divisor != 0.0f) mv = div_rn(mv, divisor);
             atomic_max_nonneg(out + col, mv);
         }
     }
+}
+
+struct NoPre {
+    __device__ void operator()() const {}
+};
+
+template <bool kBf16, bool kVec, bool kScaled>
+__global__ __launch_bounds__(256) void absmax_cols_kernel(const void* __restrict__ a, int64_t R, int64_t C,
+                                                          const float* __restrict__ row_scale, float divisor,
+                                                          float* __restrict__ out) {
+    __shared__ float part[4][kColsPerWave];
+    const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kRowsPerBlock;
+    cols_body<kBf16, kVec, kScaled>(a, R, C, kScaled ? row_scale + r0 : nullptr, divisor, out, blockIdx.x, blockIdx.y,
+                                    part, NoPre{});
 }
 
 // s_j = ax^alpha / aw^(1-alpha).  alpha = 0.5: correctly rounded roots and division; alpha = 1 and
@@ -105,11 +130,11 @@ __device__ __forceinline__ float smooth_factor(float a, float b, float alpha) {
 // ax is complete when this kernel starts (the column maxima are computed by an earlier launch on
 // the same stream).
 template <bool kBf16, bool kVec>
-__global__ __launch_bounds__(256) void absmax_rows_kernel(const void* __restrict__ a, int64_t R, int64_t C,
-                                                          float* __restrict__ out, const float* __restrict__ ax,
-                                                          float alpha, float* __restrict__ s) {
+__device__ __forceinline__ void rows_body(const void* __restrict__ a, int64_t R, int64_t C, float* __restrict__ out,
+                                          const float* __restrict__ ax, float alpha, float* __restrict__ s,
+                                          int64_t bx) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+    const int64_t r = bx * 4 + wave;
     if (r >= R) return;
     const int64_t last = kVec ? C - 8 : C - 1;
     float m = 0.0f;
@@ -130,6 +155,55 @@ __global__ __launch_bounds__(256) void absmax_rows_kernel(const void* __restrict
         out[r] = m;
         if (ax) s[r] = smooth_factor(ax[r], m, alpha);
     }
+}
+
+template <bool kBf16, bool kVec>
+__global__ __launch_bounds__(256) void absmax_rows_kernel(const void* __restrict__ a, int64_t R, int64_t C,
+                                                          float* __restrict__ out, const float* __restrict__ ax,
+                                                          float alpha, float* __restrict__ s) {
+    rows_body<kBf16, kVec>(a, R, C, out, ax, alpha, s, blockIdx.x);
+}
+
+// ---- the calibration and fold passes of one layer, fused by launch ----------------------------
+// The column maxima of X and the row maxima of W read different tensors and depend on nothing, so
+// one launch runs both: blocks [0, nx) are column blocks of X (gx across, by rows), merged into the
+// zeroed ax with atomic maxima, the rest row blocks of W.  X rows must be whole 16-byte chunks
+// (K % 8 == 0) and so must W rows (N % 8 == 0).  (Partial maxima reduced by the next launch instead
+// of the zeroing launch and the atomics were measured slower: the fold's blocks then read them.)
+template <bool kBf16>
+__global__ __launch_bounds__(256) void calib_pair_kernel(const void* __restrict__ x, int64_t M, int64_t K,
+                                                         const void* __restrict__ w, int64_t N, float* __restrict__ ax,
+                                                         float* __restrict__ aw, unsigned gx, unsigned nx) {
+    __shared__ float part[4][kColsPerWave];
+    if (blockIdx.x < nx)
+        cols_body<kBf16, true, false>(x, M, K, nullptr, 0.0f, ax, blockIdx.x % gx, blockIdx.x / gx, part, NoPre{});
+    else
+        rows_body<kBf16, true>(w, K, N, aw, nullptr, 0.0f, nullptr, blockIdx.x - nx);
+}
+
+// Column maxima of W~ = s W divided by Q (the weight scales, merged into the zeroed w_scale with
+// atomic maxima), with s[j] = smooth_factor(ax[j], aw[j]) computed by each block for its own rows
+// while its loads are in flight; the blocks of the first column block also write s.  ax and aw are
+// complete (an earlier launch on the stream).
+template <bool kBf16>
+__global__ __launch_bounds__(256) void fold_cols_kernel(const void* __restrict__ w, int64_t K, int64_t N,
+                                                        const float* __restrict__ ax, const float* __restrict__ aw,
+                                                        float alpha, float divisor, float* __restrict__ s,
+                                                        float* __restrict__ w_scale) {
+    __shared__ float part[4][kColsPerWave];
+    __shared__ float srow[kRowsPerBlock];
+    const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kRowsPerBlock;
+    auto pre = [&]() {
+        if (threadIdx.x < kRowsPerBlock) {
+            const int64_t j = r0 + threadIdx.x;
+            const int64_t jc = j < K ? j : K - 1;
+            const float sv = smooth_factor(ax[jc], aw[jc], alpha);
+            srow[threadIdx.x] = sv;
+            if (blockIdx.x == 0 && j < K) s[j] = sv;
+        }
+        __syncthreads();
+    };
+    cols_body<kBf16, true, true>(w, K, N, srow, divisor, w_scale, blockIdx.x, blockIdx.y, part, pre);
 }
 
 __global__ void smooth_factors_kernel(const float* __restrict__ ax, const float* __restrict__ aw, int64_t K,
@@ -186,6 +260,39 @@ void cols_launch(dim3 grid, const void* a, int64_t R, int64_t C, const float* ro
 }
 
 }  // namespace
+
+hipError_t launch_zero2(float* p, int64_t n, float* q, int64_t m, hipStream_t st) {
+    if (n + m <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zero2_kernel, dim3(static_cast<unsigned>((n + m + 255) / 256)), dim3(256), 0, st, p, n, q, m);
+    return hipGetLastError();
+}
+
+hipError_t launch_calib_pair(const void* x, const void* w, bool bf16, int64_t M, int64_t K, int64_t N, float* ax,
+                             float* aw, hipStream_t st) {
+    const int64_t gx = (K + kColsPerWave - 1) / kColsPerWave;
+    const int64_t nx = gx * ((M + kRowsPerBlock - 1) / kRowsPerBlock);
+    const int64_t nw = (K + 3) / 4;
+    const dim3 grid(static_cast<unsigned>(nx + nw));
+    if (bf16)
+        hipLaunchKernelGGL(calib_pair_kernel<true>, grid, dim3(256), 0, st, x, M, K, w, N, ax, aw,
+                           static_cast<unsigned>(gx), static_cast<unsigned>(nx));
+    else
+        hipLaunchKernelGGL(calib_pair_kernel<false>, grid, dim3(256), 0, st, x, M, K, w, N, ax, aw,
+                           static_cast<unsigned>(gx), static_cast<unsigned>(nx));
+    return hipGetLastError();
+}
+
+hipError_t launch_fold_cols(const void* w, bool bf16, int64_t K, int64_t N, const float* ax, const float* aw,
+                            float alpha, float divisor, float* s, float* w_scale, hipStream_t st) {
+    const dim3 grid(static_cast<unsigned>((N + kColsPerWave - 1) / kColsPerWave),
+                    static_cast<unsigned>((K + kRowsPerBlock - 1) / kRowsPerBlock));
+    if (bf16)
+        hipLaunchKernelGGL(fold_cols_kernel<true>, grid, dim3(256), 0, st, w, K, N, ax, aw, alpha, divisor, s, w_scale);
+    else
+        hipLaunchKernelGGL(fold_cols_kernel<false>, grid, dim3(256), 0, st, w, K, N, ax, aw, alpha, divisor, s,
+                           w_scale);
+    return hipGetLastError();
+}
 
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t st) {
     if (n <= 0) return hipSuccess;

@@ -21,6 +21,27 @@ hipError_t launch_absmax_cols(const void* a, bool bf16, int64_t R, int64_t C, co
 hipError_t launch_absmax_rows(const void* a, bool bf16, int64_t R, int64_t C, float* out, const float* ax,
                               float alpha, float* s, hipStream_t st);
 
+// Zero p[0, n) and q[0, m) in one launch.
+hipError_t launch_zero2(float* p, int64_t n, float* q, int64_t m, hipStream_t st);
+
+// One launch for the two calibration reductions of a layer: ax[k] = max(ax[k], max_m |X[m, k]|)
+// (atomic, ax zeroed beforehand) and aw[k] = max_n |W[k, n]|.  X, W of one dtype, K % 8 == 0,
+// N % 8 == 0, M, N >= 1.
+hipError_t launch_calib_pair(const void* x, const void* w, bool bf16, int64_t M, int64_t K, int64_t N, float* ax,
+                             float* aw, hipStream_t st);
+
+// w_scale[n] = max(w_scale[n], max_k |s[k] W[k, n]| / divisor) (atomic, w_scale zeroed
+// beforehand) with s[k] = smoothing factor of (ax[k], aw[k]) computed in the kernel, which also
+// writes s.  N % 8 == 0.
+hipError_t launch_fold_cols(const void* w, bool bf16, int64_t K, int64_t N, const float* ax, const float* aw,
+                            float alpha, float divisor, float* s, float* w_scale, hipStream_t st);
+
+// One launch for the activation codes (as launch_quant_act with s) and the weight codes (as
+// launch_quant_weight_t with per-column scales).  K <= 8192, N % 8 == 0, M, N >= 1.
+hipError_t launch_quant_pair(const void* x, bool bf16, int64_t M, int64_t K, const float* s, bool fp8, uint8_t* xq,
+                             float* x_scale, const void* w, int64_t N, const float* w_scale, uint8_t* wq,
+                             hipStream_t st);
+
 // s[j] = ax[j]^alpha / aw[j]^(1-alpha), s = 1 where a maximum is 0.
 hipError_t launch_smooth_factors(const float* ax, const float* aw, int64_t K, float alpha, float* s,
                                  hipStream_t st);

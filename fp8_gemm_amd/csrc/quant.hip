@@ -85,12 +85,13 @@ __device__ __forceinline__ void store_codes(const float (&v)[kChunks][8], float 
     }
 }
 
+// The body of a block (index bx) of kActWaves waves.  sh: kSmooth: s then 1/s, each K floats
+// (lds_half order); xchg: kSplit > 1: the parts' maxima of a row.
 template <bool kBf16, bool kFp8, int kChunks, bool kSmooth, int kSplit>
-__global__ __launch_bounds__(kActWaves * kWave) void quant_act_kernel(
-    const void* __restrict__ x, const float* __restrict__ s, int64_t M, int64_t K, int rows_per_wave,
-    uint8_t* __restrict__ q, float* __restrict__ scale) {
-    extern __shared__ float sh[];               // kSmooth: s then 1/s, each K floats (lds_half order)
-    __shared__ float xchg[2][kActWaves];        // kSplit > 1: the parts' maxima of a row
+__device__ __forceinline__ void quant_act_body(const void* __restrict__ x, const float* __restrict__ s, int64_t M,
+                                               int64_t K, int rows_per_wave, uint8_t* __restrict__ q,
+                                               float* __restrict__ scale, int64_t bx, float* sh,
+                                               float (*xchg)[kActWaves]) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int64_t nchunk = K / 8;
     float* const sh_s = sh;
@@ -103,12 +104,12 @@ __global__ __launch_bounds__(kActWaves * kWave) void quant_act_kernel(
         float sv[kPer];
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
-            const int64_t j = threadIdx.x + static_cast<int64_t>(i) * blockDim.x;
+            const int64_t j = threadIdx.x + static_cast<int64_t>(i) * (kActWaves * kWave);
             sv[i] = s[j < K ? j : K - 1];
         }
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
-            const int64_t j = threadIdx.x + static_cast<int64_t>(i) * blockDim.x;
+            const int64_t j = threadIdx.x + static_cast<int64_t>(i) * (kActWaves * kWave);
             if (j < K) {
                 const int h = lds_half(j, nchunk);
                 sh_s[h] = sv[i];
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(kActWaves * kWave) void quant_act_kernel(
     const int lane_c = part * kWave + lane;     // first chunk of this wave's share
     constexpr int kStride = kSplit * kWave;
     for (int rr = 0; rr < rows_per_wave; ++rr) {
-        const int64_t row = (static_cast<int64_t>(blockIdx.x) * rows_per_wave + rr) * kRowsPerPass + slot;
+        const int64_t row = (bx * rows_per_wave + rr) * kRowsPerPass + slot;
         const bool live = row < M;
         if (kSplit == 1 && !live) break;
         const int64_t rrow = live ? row : M - 1;
@@ -167,6 +168,15 @@ __global__ __launch_bounds__(kActWaves * kWave) void quant_act_kernel(
             store_codes<kFp8, false>(v, sc, 0.0f, lane_c, kStride, nchunk, qrow);
         }
     }
+}
+
+template <bool kBf16, bool kFp8, int kChunks, bool kSmooth, int kSplit>
+__global__ __launch_bounds__(kActWaves * kWave) void quant_act_kernel(
+    const void* __restrict__ x, const float* __restrict__ s, int64_t M, int64_t K, int rows_per_wave,
+    uint8_t* __restrict__ q, float* __restrict__ scale) {
+    extern __shared__ float sh[];
+    __shared__ float xchg[2][kActWaves];
+    quant_act_body<kBf16, kFp8, kChunks, kSmooth, kSplit>(x, s, M, K, rows_per_wave, q, scale, blockIdx.x, sh, xchg);
 }
 
 // Rows longer than the register-resident variants (K > 8192): two passes over the row (the second
@@ -301,29 +311,40 @@ __device__ __forceinline__ void code_item(const WeightItem<kBf16, kVec>& it, con
     }
 }
 
+// LDS of one weight tile.
+struct WeightTileLds {
+    uint32_t tile[kTN * kTStride];
+    float col_scale[kTN], col_rcp[kTN], row_s[kTJ];
+};
+
+// The body of one tile (bx, by) = (column tile, row tile), run by 256 threads with index tid.  Its
+// barriers are block-wide, so every thread of the block runs it (a second tile of a 512-thread
+// block, or an inactive one that loads and codes a valid tile and stores nothing).
 template <bool kBf16, bool kFp8, bool kVec>
-__global__ __launch_bounds__(256) void quant_weight_t_kernel(const void* __restrict__ w, int64_t K, int64_t N,
-                                                             const float* __restrict__ s,
-                                                             const float* __restrict__ w_scale, int64_t scale_step,
-                                                             uint8_t* __restrict__ wq) {
-    __shared__ uint32_t tile[kTN * kTStride];
-    __shared__ float col_scale[kTN], col_rcp[kTN], row_s[kTJ];
-    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kTN;
-    const int64_t j0 = static_cast<int64_t>(blockIdx.y) * kTJ;
+__device__ __forceinline__ void weight_tile_body(const void* __restrict__ w, int64_t K, int64_t N,
+                                                 const float* __restrict__ s, const float* __restrict__ w_scale,
+                                                 int64_t scale_step, uint8_t* __restrict__ wq, int64_t bx, int64_t by,
+                                                 int tid, bool active, WeightTileLds& L) {
+    uint32_t* const tile = L.tile;
+    float* const col_scale = L.col_scale;
+    float* const col_rcp = L.col_rcp;
+    float* const row_s = L.row_s;
+    const int64_t n0 = bx * kTN;
+    const int64_t j0 = by * kTJ;
     bool fast = true;
-    if (threadIdx.x < kTN) {
-        const int64_t n = n0 + threadIdx.x;
+    if (tid < kTN) {
+        const int64_t n = n0 + tid;
         const float sc = (n < N) ? w_scale[n * scale_step] : 0.0f;
-        col_scale[threadIdx.x] = sc;
-        col_rcp[threadIdx.x] = div_rn(1.0f, sc);
+        col_scale[tid] = sc;
+        col_rcp[tid] = div_rn(1.0f, sc);
         fast = sc == 0.0f || in_pow2_range<-60, 60>(sc);
     }
     {
-        const int64_t j = j0 + threadIdx.x;
-        row_s[threadIdx.x] = (s && j < K) ? s[j] : 1.0f;
+        const int64_t j = j0 + tid;
+        row_s[tid] = (s && j < K) ? s[j] : 1.0f;
     }
     fast = __syncthreads_and(fast);
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int wave = tid / kWave, lane = tid % kWave;
     const int cl = lane & 7, rl = lane >> 3;
     // kTJ / 4 row groups x kTN / 8 column chunks, kItems (group, chunk) items per thread.  Item it of
     // wave w is combination b = kItems w + it: column chunk cc = cl + 8 (b / (kTJ / 32)), row group
@@ -346,11 +367,47 @@ __global__ __launch_bounds__(256) void quant_weight_t_kernel(const void* __restr
     __syncthreads();
     // Row n0 + c of wq gets 16-byte piece t (tile rows 16 t .. 16 t + 15 = row groups 4 t .. 4 t + 3,
     // stored at word 4 (t ^ 2 ((c / 8) % 8))).  16 consecutive threads read one column's 256 bytes.
-    for (int idx = threadIdx.x; idx < kTN * (kTJ / 16); idx += blockDim.x) {
+    for (int idx = tid; idx < kTN * (kTJ / 16); idx += 256) {
         const int c = idx / (kTJ / 16), t = idx % (kTJ / 16);
         const int64_t n = n0 + c, j = j0 + 16 * t;
         const uint4 u = *reinterpret_cast<const uint4*>(&tile[c * kTStride + 4 * (t ^ (2 * ((c >> 3) & 7)))]);
-        if (n < N && j < K) *reinterpret_cast<uint4*>(wq + n * K + j) = u;   // K % 16 == 0
+        if (active && n < N && j < K) *reinterpret_cast<uint4*>(wq + n * K + j) = u;   // K % 16 == 0
+    }
+}
+
+template <bool kBf16, bool kFp8, bool kVec>
+__global__ __launch_bounds__(256) void quant_weight_t_kernel(const void* __restrict__ w, int64_t K, int64_t N,
+                                                             const float* __restrict__ s,
+                                                             const float* __restrict__ w_scale, int64_t scale_step,
+                                                             uint8_t* __restrict__ wq) {
+    __shared__ WeightTileLds L;
+    weight_tile_body<kBf16, kFp8, kVec>(w, K, N, s, w_scale, scale_step, wq, blockIdx.x, blockIdx.y, threadIdx.x, true,
+                                        L);
+}
+
+// ---- the activation and weight codes of one layer in one launch -------------------------------
+// Both need only s and the final weight scales, so blocks [0, nq) quantize activations (as
+// quant_act_kernel) and the others code two weight tiles each (as quant_weight_t_kernel, waves 0-3
+// and 4-7); tile 2b + 1 past the last tile is inactive.  One dynamic LDS buffer serves either role.
+template <bool kBf16, bool kFp8, int kChunks, int kSplit>
+__global__ __launch_bounds__(kActWaves * kWave) void quant_pair_kernel(
+    const void* __restrict__ x, const float* __restrict__ s, int64_t M, int64_t K, int rows_per_wave,
+    uint8_t* __restrict__ xq, float* __restrict__ x_scale, const void* __restrict__ w, int64_t N,
+    const float* __restrict__ w_scale, uint8_t* __restrict__ wq, unsigned nq, unsigned wtx, unsigned ntiles) {
+    extern __shared__ float4 lds4[];
+    if (blockIdx.x < nq) {
+        float* const sh = reinterpret_cast<float*>(lds4);
+        float (*xchg)[kActWaves] = reinterpret_cast<float (*)[kActWaves]>(sh + 2 * K);
+        quant_act_body<kBf16, kFp8, kChunks, true, kSplit>(x, s, M, K, rows_per_wave, xq, x_scale, blockIdx.x, sh,
+                                                           xchg);
+    } else {
+        const int half = threadIdx.x / 256;
+        WeightTileLds* const L = reinterpret_cast<WeightTileLds*>(lds4) + half;
+        const unsigned t = 2 * (blockIdx.x - nq) + half;
+        const bool active = t < ntiles;
+        const unsigned tc = active ? t : ntiles - 1;
+        weight_tile_body<kBf16, kFp8, true>(w, K, N, s, w_scale, 1, wq, tc % wtx, tc / wtx, threadIdx.x % 256, active,
+                                            *L);
     }
 }
 
@@ -620,6 +677,37 @@ hipError_t quant_act_dispatch(const void* x, int64_t M, int64_t K, const float* 
     return hipGetLastError();
 }
 
+template <bool kBf16, bool kFp8, int kChunks, int kSplit>
+void quant_pair_launch(const void* x, int64_t M, int64_t K, const float* s, uint8_t* xq, float* xs, const void* w,
+                       int64_t N, const float* w_scale, uint8_t* wq, hipStream_t st) {
+    const int64_t rows_per_pass = kActWaves / kSplit;
+    const int64_t rows_per_block_pass = rows_per_pass * 512;
+    const int rpw = static_cast<int>(std::max<int64_t>(1, (M + rows_per_block_pass - 1) / rows_per_block_pass));
+    const int64_t rows_per_block = rows_per_pass * rpw;
+    const int64_t nq = (M + rows_per_block - 1) / rows_per_block;
+    const int64_t wtx = (N + kTN - 1) / kTN;
+    const int64_t ntiles = wtx * ((K + kTJ - 1) / kTJ);
+    const size_t lds = std::max(2 * static_cast<size_t>(K) * sizeof(float) + 2 * kActWaves * sizeof(float),
+                                2 * sizeof(WeightTileLds));
+    hipLaunchKernelGGL((quant_pair_kernel<kBf16, kFp8, kChunks, kSplit>), dim3(static_cast<unsigned>(nq + (ntiles + 1) / 2)),
+                       dim3(kActWaves * kWave), lds, st, x, s, M, K, rpw, xq, xs, w, N, w_scale, wq,
+                       static_cast<unsigned>(nq), static_cast<unsigned>(wtx), static_cast<unsigned>(ntiles));
+}
+
+// K <= 8192, N % 8 == 0, M, N >= 1.
+template <bool kBf16, bool kFp8>
+hipError_t quant_pair_dispatch(const void* x, int64_t M, int64_t K, const float* s, uint8_t* xq, float* xs,
+                               const void* w, int64_t N, const float* w_scale, uint8_t* wq, hipStream_t st) {
+    const int64_t per_lane = (K / 8 + kWave - 1) / kWave;
+    if (per_lane <= 1) quant_pair_launch<kBf16, kFp8, 1, 1>(x, M, K, s, xq, xs, w, N, w_scale, wq, st);
+    else if (per_lane <= 2) quant_pair_launch<kBf16, kFp8, 2, 1>(x, M, K, s, xq, xs, w, N, w_scale, wq, st);
+    else if (per_lane <= 4) quant_pair_launch<kBf16, kFp8, 4, 1>(x, M, K, s, xq, xs, w, N, w_scale, wq, st);
+    else if (per_lane <= 8) quant_pair_launch<kBf16, kFp8, 4, 2>(x, M, K, s, xq, xs, w, N, w_scale, wq, st);
+    else if (per_lane <= 16) quant_pair_launch<kBf16, kFp8, 4, 4>(x, M, K, s, xq, xs, w, N, w_scale, wq, st);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 template <bool kBf16, bool kFp8>
 hipError_t quant_weight_dispatch(const void* w, int64_t K, int64_t N, const float* s, const float* w_scale,
                                  int64_t scale_step, uint8_t* wq, hipStream_t st) {
@@ -748,6 +836,15 @@ hipError_t launch_quant_weight_t(const void* w, bool bf16, int64_t K, int64_t N,
                          : quant_weight_dispatch<true, false>(w, K, N, s, w_scale, step, wq, st);
     return fp8 ? quant_weight_dispatch<false, true>(w, K, N, s, w_scale, step, wq, st)
                : quant_weight_dispatch<false, false>(w, K, N, s, w_scale, step, wq, st);
+}
+
+hipError_t launch_quant_pair(const void* x, bool bf16, int64_t M, int64_t K, const float* s, bool fp8, uint8_t* xq,
+                             float* x_scale, const void* w, int64_t N, const float* w_scale, uint8_t* wq,
+                             hipStream_t st) {
+    if (bf16) return fp8 ? quant_pair_dispatch<true, true>(x, M, K, s, xq, x_scale, w, N, w_scale, wq, st)
+                         : quant_pair_dispatch<true, false>(x, M, K, s, xq, x_scale, w, N, w_scale, wq, st);
+    return fp8 ? quant_pair_dispatch<false, true>(x, M, K, s, xq, x_scale, w, N, w_scale, wq, st)
+               : quant_pair_dispatch<false, false>(x, M, K, s, xq, x_scale, w, N, w_scale, wq, st);
 }
 
 hipError_t launch_quant_tensor(const void* a, bool bf16, int64_t n, const float* amax_in, bool fp8, uint8_t* q,

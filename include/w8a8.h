@@ -98,6 +98,21 @@ w8a8_status w8a8_quant_act(const void* x, w8a8_dtype x_dtype, int64_t M, int64_t
                            hipStream_t stream);
 
 /*
+ * Calibration, smoothing factors, weight fold + quantize and activation quantize of one layer in
+ * one call ([WAQ] s3 steps 1 and 2, the calibration of s3 "Choosing the Smoothing Factor"): the
+ * results are those of w8a8_smooth_scales (accumulate = 0), then w8a8_fold_quant_weight with its
+ * s, then w8a8_quant_act with its s, bit for bit.  ax, aw, s: fp32 [K]; wq [N, K], w_scale [N];
+ * xq [M, K], x_scale [M]; all written, and none may overlap x or w.  X and W of one dtype,
+ * N % 8 == 0 and K <= 8192 take four launches (zero ax and w_scale; both calibration maxima; s
+ * and the weight scales; the activation and weight codes); other shapes take the three calls'
+ * seven.  Errors as the three calls.
+ */
+w8a8_status w8a8_smooth_quant(const void* x, w8a8_dtype x_dtype, int64_t M, int64_t K,
+                              const void* w, w8a8_dtype w_dtype, int64_t N, float alpha,
+                              w8a8_qtype qtype, float* ax, float* aw, float* s, void* wq,
+                              float* w_scale, void* xq, float* x_scale, hipStream_t stream);
+
+/*
  * Quantized GEMM with the dequantizing epilogue ([WAQ] s3 "Y = dequantize(X_int8 @ W_int8)";
  * [WAQ] s4 x^ = s q for E4M3).
  *   INT8: acc[i, n] = sum_k xq[i, k] * wq[n, k] exactly in int32 (|acc| <= K * 127^2, so

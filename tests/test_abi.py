@@ -19,7 +19,8 @@ def declared_functions():
 
 def test_header_declares_the_path():
     names = declared_functions()
-    for fn in ("w8a8_smooth_scales", "w8a8_fold_quant_weight", "w8a8_quant_act", "w8a8_gemm_dequant",
+    for fn in ("w8a8_smooth_scales", "w8a8_fold_quant_weight", "w8a8_quant_act", "w8a8_smooth_quant",
+               "w8a8_gemm_dequant",
                "w8a8_gemm_i32", "w8a8_status_string", "w8a8_version"):
         assert fn in names
 
@@ -72,6 +73,21 @@ def test_argument_validation_without_gpu():
     assert L.w8a8_smooth_scales(fake, 1, 4, 16, fake, 1, 8, -0.1, fake, fake, 0, fake, None) == INV
     assert L.w8a8_smooth_scales(fake, 1, 4, 16, fake, 1, 8, float("nan"), fake, fake, 0, fake, None) == INV
     assert L.w8a8_smooth_scales(fake, 1, 4, 16, fake, 1, 8, 0.5, None, fake, 0, fake, None) == INV
+    # smooth_quant (x, xt, M, K, w, wt, N, alpha, qtype, ax, aw, s, wq, w_scale, xq, x_scale, stream)
+    assert L.w8a8_smooth_quant(fake, 1, 4, 16, fake, 1, 8, 2.0, 0, fake, fake, fake, fake, fake, fake, fake,
+                               None) == INV                                             # alpha > 1
+    assert L.w8a8_smooth_quant(fake, 1, 4, 16, fake, 1, 8, 0.5, 4, fake, fake, fake, fake, fake, fake, fake,
+                               None) == INV                                             # bad qtype
+    assert L.w8a8_smooth_quant(fake, 1, 4, 16, fake, 1, 8, 0.5, 0, fake, fake, None, fake, fake, fake, fake,
+                               None) == INV                                             # NULL s
+    assert L.w8a8_smooth_quant(fake, 1, 4, 16, fake, 1, 8, 0.5, 0, fake, fake, fake, None, fake, fake, fake,
+                               None) == INV                                             # NULL wq
+    assert L.w8a8_smooth_quant(fake, 1, 4, 16, fake, 1, 8, 0.5, 0, fake, fake, fake, fake, fake, None, fake,
+                               None) == INV                                             # NULL xq
+    assert L.w8a8_smooth_quant(fake, 1, 4, 40, fake, 1, 8, 0.5, 0, fake, fake, fake, fake, fake, fake, fake,
+                               None) == UNS                                             # K % 16
+    assert L.w8a8_smooth_quant(fake, 1, 4, 16, fake, 1, 8, 0.5, 0, fake, fake, fake, odd, fake, fake, fake,
+                               None) == UNS                                             # alignment
     # fold
     assert L.w8a8_fold_quant_weight(None, 1, 16, 8, None, 0, fake, fake, None) == INV
     assert L.w8a8_fold_quant_weight(fake, 1, 16, 0, None, 0, None, None, None) == OK
