@@ -111,3 +111,29 @@ def test_smooth_quant_repeated_calls(f):
     np.testing.assert_array_equal(host(out["ax"]), ax)
     _, sw = oracle.fold_quant_weight(W2, s, "int8")
     np.testing.assert_array_equal(host(out["w_scale"]), sw)
+
+
+@pytest.mark.parametrize("M,N", [(0, 64), (24, 0)])
+def test_smooth_quant_empty(f, M, N):
+    """No activation rows (ax = 0) or no weight columns (aw = 0): s = 1 everywhere, and the outputs
+    that exist match the oracle."""
+    announce(f"smooth_quant empty M={M} N={N}")
+    K = 512
+    X = synth.random_matrix((M, K), seed=3) if M else np.zeros((0, K), np.float32)
+    W = synth.random_matrix((K, N), seed=4, scale=0.02) if N else np.zeros((K, 0), np.float32)
+    X, W = synth.f32_to_bf16_bits(X), synth.f32_to_bf16_bits(W)
+    r = f.w8a8_smooth_quant(dev(X), dev(W), 0.5, "int8")
+    torch.cuda.synchronize()
+    ax, aw, s = oracle.smooth_scales(X, W, 0.5)
+    np.testing.assert_array_equal(host(r["ax"]), ax)
+    np.testing.assert_array_equal(host(r["aw"]), aw)
+    np.testing.assert_array_equal(host(r["s"]), s)
+    assert np.all(s == 1.0)
+    if N:
+        qw, sw = oracle.fold_quant_weight(W, s, "int8")
+        np.testing.assert_array_equal(host(r["w_scale"]), sw)
+        np.testing.assert_array_equal(codes(host(r["wq"])), codes(qw))
+    if M:
+        qx, sx = oracle.quant_act(X, s, "int8")
+        np.testing.assert_array_equal(host(r["x_scale"]), sx)
+        np.testing.assert_array_equal(codes(host(r["xq"])), codes(qx))
