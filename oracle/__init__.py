@@ -61,6 +61,8 @@ def _load():
         "oracle_fold_norm_gain": (None, [P, P, I64, P]),
         "oracle_rms_norm": (None, [P, I, I64, I64, P, F, P]),
         "oracle_norm_quant_act": (I, [P, I, I64, I64, P, F, I, P, P]),
+        "oracle_layer_norm": (None, [P, I, I64, I64, P, P, F, P]),
+        "oracle_layer_norm_quant_act": (I, [P, I, I64, I64, P, P, F, I, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -394,4 +396,29 @@ def norm_quant_act(h, g=None, eps=1e-5, qtype="int8"):
     if lib.oracle_norm_quant_act(_ptr(h), dt, M, K, _ptr(_f32(g)), float(np.float32(eps)), q, _ptr(codes),
                                  _ptr(sx)) != 0:
         raise MemoryError("oracle_norm_quant_act")
+    return _codes(codes, q), sx
+
+
+def layer_norm(h, g=None, b=None, eps=1e-5):
+    """((h[j] - mu) * r) * g[j] + b[j] per row, mu and the variance about it rounded to float once:
+    float32 [M, K]."""
+    h, dt = _input(h)
+    M, K = h.shape
+    out = np.empty((M, K), np.float32)
+    _load().oracle_layer_norm(_ptr(h), dt, M, K, _ptr(_f32(g)), _ptr(_f32(b)), float(np.float32(eps)), _ptr(out))
+    return out
+
+
+def layer_norm_quant_act(h, g=None, b=None, eps=1e-5, qtype="int8"):
+    """LayerNorm with gain g and bias b (1/s folded into both), then per-token quantize:
+    (codes [M, K], scales [M])."""
+    lib = _load()
+    q = qtype_code(qtype)
+    h, dt = _input(h)
+    M, K = h.shape
+    codes = np.empty((M, K), np.uint8)
+    sx = np.empty(M, np.float32)
+    if lib.oracle_layer_norm_quant_act(_ptr(h), dt, M, K, _ptr(_f32(g)), _ptr(_f32(b)), float(np.float32(eps)), q,
+                                       _ptr(codes), _ptr(sx)) != 0:
+        raise MemoryError("oracle_layer_norm_quant_act")
     return _codes(codes, q), sx

@@ -37,7 +37,9 @@
  *     sum, and the reference is that sum in double (the dequantized weight is not rounded first);
  *   - with the smoothing folded offline into the layer before, that layer is an RMS norm
  *     (x * r) * g with r = 1 / sqrt(mean(x^2) + eps), the mean taken in double and rounded to
- *     float once, and 1/s folded into its gain g' = g / s.
+ *     float once, and 1/s folded into its gain g' = g / s; or a LayerNorm
+ *     ((x - mu) * r) * g' + b' with mu and the variance about it each rounded to float once, and
+ *     1/s folded into both gain and bias.
  *
  * Arithmetic: IEEE binary32/binary64, round-to-nearest-even, compiled without fast-math and
  * without FMA contraction.  Every loop is the definition written out; the only parallelism is an
@@ -464,6 +466,51 @@ int oracle_norm_quant_act(const void* h, int dtype, int64_t M, int64_t K, const 
     float* xs = (float*)malloc(sizeof(float) * (size_t)(M * K > 0 ? M * K : 1));
     if (!xs) return -1;
     oracle_rms_norm(h, dtype, M, K, g, eps, xs);
+    oracle_quantize_rows(xs, M, K, qtype, q, sx);
+    free(xs);
+    return 0;
+}
+
+/* ---- LayerNorm with the smoothing folded into its gain and bias ----------------------------
+ * The same offline fold when the norm before the layer is a LayerNorm: both its gain and its bias
+ * scale the output, so both are divided by s (b'[j] = b[j] / s[j], the division of
+ * oracle_fold_norm_gain).  Per row of h [M, K]:
+ *   mu    = (float)((sum_j (double)h[j]) / K)               (the sum carried in double-double)
+ *   d[j]  = h[j] - mu                                       (fp32)
+ *   var   = (float)((sum_j (double)d[j] * d[j]) / K)        (the sum carried in double-double)
+ *   r     = 1 / sqrtf(var + eps)
+ *   X~[j] = (d[j] * r) * g'[j] + b'[j]                      (fp32 multiply, multiply, add, in this
+ *                                                            order; no fused multiply-add)
+ * g == NULL: g = 1; b == NULL: b = 0.  The variance is taken about the rounded mean (two passes),
+ * not as mean(h^2) - mu^2.
+ * ------------------------------------------------------------------------------------------- */
+void oracle_layer_norm(const void* h, int dtype, int64_t M, int64_t K, const float* g, const float* b, float eps,
+                       float* out) {
+    for (int64_t m = 0; m < M; ++m) {
+        double hi = 0.0, lo = 0.0;
+        for (int64_t j = 0; j < K; ++j) dd_add(&hi, &lo, (double)load_elem(h, dtype, m * K + j));
+        const float mu = (float)((hi + lo) / (double)K);
+        hi = 0.0;
+        lo = 0.0;
+        for (int64_t j = 0; j < K; ++j) {
+            const float d = load_elem(h, dtype, m * K + j) - mu;
+            dd_add(&hi, &lo, (double)d * (double)d);
+        }
+        const float var = (float)((hi + lo) / (double)K);
+        const float r = 1.0f / sqrtf(var + eps);
+        for (int64_t j = 0; j < K; ++j) {
+            const float d = load_elem(h, dtype, m * K + j) - mu;
+            const float t = (d * r) * (g ? g[j] : 1.0f);
+            out[m * K + j] = t + (b ? b[j] : 0.0f);
+        }
+    }
+}
+
+int oracle_layer_norm_quant_act(const void* h, int dtype, int64_t M, int64_t K, const float* g, const float* b,
+                                float eps, int qtype, uint8_t* q, float* sx) {
+    float* xs = (float*)malloc(sizeof(float) * (size_t)(M * K > 0 ? M * K : 1));
+    if (!xs) return -1;
+    oracle_layer_norm(h, dtype, M, K, g, b, eps, xs);
     oracle_quantize_rows(xs, M, K, qtype, q, sx);
     free(xs);
     return 0;

@@ -168,3 +168,25 @@ def mean_square_tie_rows(K: int) -> np.ndarray:
     small = [1, 3, 4, 5, 6, 7]
     rows[1, small] = 2.0 ** -24
     return rows
+
+
+def mean_tie_rows(K: int) -> np.ndarray:
+    """Two float32 rows of length K (a power of two, >= 16) whose sum is 128 + 2^-17, so their mean
+    (128 + 2^-17) / K lies exactly halfway between two adjacent floats; row 1 adds six terms 2^-48
+    after the 128 in its first 8 elements.  Each is below half an ulp of the running sum there, so a
+    sequential double sum drops them, but together they exceed half an ulp of 128 in double, so the
+    exact sum, rounded to double, and its mean lie just past the halfway point."""
+    assert K >= 16 and K & (K - 1) == 0
+    rows = np.zeros((2, K), np.float32)
+    rows[:, 0] = 128.0
+    rows[:, 1] = 2.0 ** -17
+    rows[1, 2:8] = 2.0 ** -48
+    return rows
+
+
+def variance_tie_rows(K: int) -> np.ndarray:
+    """Two float32 rows of length K (a power of two, >= 32) with mean exactly 0 (each value and its
+    negation) whose mean square is that of mean_square_tie_rows(K // 2): a float tie in row 0 and
+    just past it, through squares a sequential double sum drops, in row 1."""
+    t = mean_square_tie_rows(K // 2)
+    return np.concatenate([t, -t], axis=1)

@@ -320,3 +320,129 @@ def test_rms_norm_mean_square_tie(K):
         np.testing.assert_array_equal(y[r], (h[r] * rr).astype(np.float32))
     assert np.float32(seq / K) == np.float32(math.fsum(float(v) * float(v) for v in h[0]) / K)
     assert y[0, 0] != y[1, 0]
+
+
+# ---- LayerNorm with the smoothing folded into gain and bias ---------------------------------
+
+def ln_ref(h, g, b, eps):
+    mu = h.mean(axis=1, keepdims=True)
+    var = ((h - mu) ** 2).mean(axis=1, keepdims=True)
+    return (h - mu) / np.sqrt(var + eps) * g[None, :] + b[None, :]
+
+
+def test_layer_norm_matches_numpy_float64():
+    """Within a few fp32 roundings of the float64 formula.  Catches: a missing mean subtraction,
+    the variance about 0 (that is RMS norm), a missing eps, the bias before the gain."""
+    h = synth.random_matrix((11, 320), seed=61, outliers=3) + np.float32(3.0)
+    g = synth.random_scales(320, seed=62, lo=0.5, hi=2.0)
+    b = synth.random_scales(320, seed=63, lo=-1.0, hi=1.0)
+    for eps in (1e-5, 0.0):
+        y = oracle.layer_norm(h, g, b, eps)
+        ref = ln_ref(h.astype(np.float64), g.astype(np.float64), b.astype(np.float64), eps)
+        np.testing.assert_allclose(y, ref, rtol=0, atol=2e-6 * np.abs(ref).max())
+
+
+def test_layer_norm_exact_cases():
+    """Closed forms: a constant row has d = 0, so X~ = b exactly; scaling a row by a power of two
+    (eps = 0) leaves the output bit-identical (the mean scales exactly, the variance by the square);
+    g = 1, b = 0 leaves a row with mean 0 and mean square 1 unchanged."""
+    g = synth.random_scales(64, seed=64, lo=0.5, hi=2.0)
+    b = synth.random_scales(64, seed=65, lo=0.25, hi=1.0)
+    h = np.full((1, 64), 3.25, np.float32)
+    np.testing.assert_array_equal(oracle.layer_norm(h, g, b, 1e-5)[0], b)
+    h = synth.random_matrix((5, 64), seed=66, outliers=1) + np.float32(2.0)
+    y = oracle.layer_norm(h, g, b, 0.0)
+    for k in (-3, 5):
+        np.testing.assert_array_equal(oracle.layer_norm(h * np.float32(2.0 ** k), g, b, 0.0), y)
+    row = np.array([[1.0, -1.0] * 32], np.float32)
+    np.testing.assert_array_equal(oracle.layer_norm(row, None, None, 0.0), row)
+
+
+def test_layer_norm_fold_and_identity():
+    """Gain and bias both divided by s (the division of fold_norm_gain): the folded norm equals the
+    norm divided by s to fp32 rounding, and (LN(h) g/s + b/s)(s W) = (LN(h) g + b) W (s3's identity).
+    Catches: folding only the gain, multiplying the bias by s."""
+    K, N = 96, 7
+    g = synth.random_scales(K, seed=67, lo=0.5, hi=2.0)
+    b = synth.random_scales(K, seed=68, lo=-0.5, hi=0.5)
+    s = synth.random_scales(K, seed=69, lo=0.1, hi=8.0)
+    gf, bf = oracle.fold_norm_gain(g, s), oracle.fold_norm_gain(b, s)
+    np.testing.assert_array_equal(bf, (b / s).astype(np.float32))
+    h = synth.random_matrix((9, K), seed=70, outliers=2)
+    W = synth.random_matrix((K, N), seed=71, scale=0.02)
+    xs = oracle.layer_norm(h, gf, bf, 1e-5).astype(np.float64)
+    x = oracle.layer_norm(h, g, b, 1e-5).astype(np.float64)
+    np.testing.assert_allclose(xs, x / s.astype(np.float64)[None, :], rtol=0, atol=2e-6 * np.abs(xs).max())
+    ws = oracle.smooth_weight(W, s).astype(np.float64)
+    ref = x @ W.astype(np.float64)
+    assert np.linalg.norm(xs @ ws - ref) <= 1e-5 * np.linalg.norm(ref)
+
+
+def test_layer_norm_two_pass_rounding_reading():
+    """The mean is the float of math.fsum(h) / K; d = h - mu is an fp32 subtraction; the variance
+    is the float of math.fsum(d^2) / K (order-free), on rows whose values span 2^40, where d is not
+    exact in fp32; reversing a row changes nothing.  Catches: d in double, a plain double sum, the
+    one-pass variance mean(h^2) - mu^2."""
+    import math
+    rng = np.random.Generator(np.random.PCG64(72))
+    h = rng.standard_normal((6, 2048)).astype(np.float32)
+    h *= np.exp2(rng.integers(-20, 20, h.shape)).astype(np.float32)
+    y = oracle.layer_norm(h, None, None, 0.0)
+    np.testing.assert_array_equal(oracle.layer_norm(h[:, ::-1].copy(), None, None, 0.0)[:, ::-1], y)
+    for r in range(6):
+        mu = np.float32(math.fsum(float(v) for v in h[r]) / 2048.0)
+        d = (h[r] - mu).astype(np.float32)
+        var = np.float32(math.fsum(float(v) * float(v) for v in d) / 2048.0)
+        rr = np.float32(1.0) / np.sqrt(var)
+        np.testing.assert_array_equal(y[r], (d * rr).astype(np.float32))
+
+
+@pytest.mark.parametrize("K", [16, 128, 1024, 8192])
+def test_layer_norm_mean_and_variance_ties(K):
+    """Rows whose mean, or whose variance, is exactly a float tie (rounds to even) or just past one
+    through terms a sequential double sum drops: the oracle takes the correctly rounded value of
+    the exact sum in both, and the two rows of each pair quantize to different scales (with a gain
+    that makes the entries at the mean set the scale)."""
+    import math
+
+    def by_fsum(row):
+        mu = np.float32(math.fsum(float(v) for v in row) / K)
+        d = (row - mu).astype(np.float32)
+        var = np.float32(math.fsum(float(v) * float(v) for v in d) / K)
+        return mu, (d * (np.float32(1.0) / np.sqrt(var))).astype(np.float32)
+
+    h = synth.mean_tie_rows(K)
+    y = oracle.layer_norm(h, None, None, 0.0)
+    mus = []
+    for r in range(2):
+        mu, ref = by_fsum(h[r])
+        mus.append(mu)
+        np.testing.assert_array_equal(y[r], ref)
+    assert mus[0] != mus[1]
+    seq = 0.0
+    for v in h[1].astype(np.float64):
+        seq += v
+    assert np.float32(seq / K) == mus[0]          # a plain sequential double sum lands on the tie
+    g = np.ones(K, np.float32)
+    g[0] = 2.0 ** -20
+    for qt in ("int8", "fp8"):
+        _, sx = oracle.layer_norm_quant_act(h, g, None, 0.0, qt)
+        assert sx[0] != sx[1]
+    if K >= 32:
+        hv = synth.variance_tie_rows(K)
+        y = oracle.layer_norm(hv, None, None, 0.0)
+        for r in range(2):
+            var = np.float32(math.fsum(float(v) * float(v) for v in hv[r]) / K)     # mean is 0 exactly
+            np.testing.assert_array_equal(y[r], (hv[r] * (np.float32(1.0) / np.sqrt(var))).astype(np.float32))
+        assert not np.array_equal(y[0], y[1])
+
+
+def test_layer_norm_quant_act_is_norm_then_per_row_quantize():
+    h = synth.random_matrix((7, 256), seed=73, outliers=2)
+    g = synth.random_scales(256, seed=74, lo=0.5, hi=2.0)
+    b = synth.random_scales(256, seed=75, lo=-0.5, hi=0.5)
+    for qt in ("int8", "fp8"):
+        q, sx = oracle.layer_norm_quant_act(h, g, b, 1e-5, qt)
+        q2, sx2 = oracle.quantize_rows(oracle.layer_norm(h, g, b, 1e-5), qt)
+        np.testing.assert_array_equal(sx, sx2)
+        np.testing.assert_array_equal(np.ascontiguousarray(q).view(np.uint8), np.ascontiguousarray(q2).view(np.uint8))
