@@ -28,7 +28,7 @@ ENTRY_POINTS = ("w8a8_smooth_scales", "w8a8_fold_quant_weight", "w8a8_quant_act"
                 "w8a8_gemm_dequant",
                 "w8a8_gemm_i32", "w8a8_gemm_f32", "w8a8_absmax", "w8a8_quant_act_tensor",
                 "w8a8_quant_weight_tensor", "w8a8_gemm_dequant_tensor", "w8a8_gemm_w8a16", "w8a8_fold_norm_gain",
-                "w8a8_norm_quant_act", "w8a8_status_string", "w8a8_version")
+                "w8a8_norm_quant_act", "w8a8_layer_norm_quant_act", "w8a8_status_string", "w8a8_version")
 
 
 class W8A8Error(RuntimeError):
@@ -63,6 +63,7 @@ def _load() -> ctypes.CDLL:
         "w8a8_gemm_w8a16": (I, [P, P, P, I64, I64, I64, P, P]),
         "w8a8_fold_norm_gain": (I, [P, P, I64, P, P]),
         "w8a8_norm_quant_act": (I, [P, I, I64, I64, P, F, I, P, P, P]),
+        "w8a8_layer_norm_quant_act": (I, [P, I, I64, I64, P, P, F, I, P, P, P]),
         "w8a8_status_string": (ctypes.c_char_p, [I]),
         "w8a8_version": (ctypes.c_char_p, []),
     }
@@ -361,4 +362,18 @@ def w8a8_norm_quant_act(h, g=None, eps: float = 1e-5, qtype="int8", xq=None, x_s
     x_scale = torch.empty(M, dtype=torch.float32, device=h.device) if x_scale is None else _dev(x_scale, "x_scale")
     _check("w8a8_norm_quant_act", _load().w8a8_norm_quant_act(
         _ptr(h), _dtype(h), M, K, _ptr(g), float(eps), q, _ptr(xq), _ptr(x_scale), _stream(stream)))
+    return xq, x_scale
+
+
+def w8a8_layer_norm_quant_act(h, g=None, b=None, eps: float = 1e-5, qtype="int8", xq=None, x_scale=None,
+                              stream=None):
+    """LayerNorm of h [M, K] with gain g and bias b (1/s folded into both), then per-token
+    quantize: (codes [M, K], scales float32 [M])."""
+    _dev(h, "h"), _dev(g, "g"), _dev(b, "b")
+    q = _qtype(qtype)
+    M, K = h.shape
+    xq = torch.empty((M, K), dtype=_code_dtype(q), device=h.device) if xq is None else _dev(xq, "xq")
+    x_scale = torch.empty(M, dtype=torch.float32, device=h.device) if x_scale is None else _dev(x_scale, "x_scale")
+    _check("w8a8_layer_norm_quant_act", _load().w8a8_layer_norm_quant_act(
+        _ptr(h), _dtype(h), M, K, _ptr(g), _ptr(b), float(eps), q, _ptr(xq), _ptr(x_scale), _stream(stream)))
     return xq, x_scale

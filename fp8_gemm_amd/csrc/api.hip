@@ -240,8 +240,24 @@ W8A8_API w8a8_status w8a8_norm_quant_act(const void* h, w8a8_dtype h_dtype, int6
     if (K > 8192) return W8A8_ERR_UNSUPPORTED;            // rows are held in registers
     if (M == 0) return W8A8_OK;
     if (!aligned16(h) || !aligned16(g) || !aligned16(xq) || !aligned16(x_scale)) return W8A8_ERR_UNSUPPORTED;
-    return from_hip(w8a8::launch_norm_quant_act(h, h_dtype == W8A8_BF16, M, K, g, eps, qtype == W8A8_FP8_E4M3,
-                                                static_cast<uint8_t*>(xq), x_scale, stream));
+    return from_hip(w8a8::launch_norm_quant_act(h, h_dtype == W8A8_BF16, M, K, g, nullptr, false, eps,
+                                                qtype == W8A8_FP8_E4M3, static_cast<uint8_t*>(xq), x_scale, stream));
+}
+
+W8A8_API w8a8_status w8a8_layer_norm_quant_act(const void* h, w8a8_dtype h_dtype, int64_t M, int64_t K, const float* g,
+                                               const float* b, float eps, w8a8_qtype qtype, void* xq, float* x_scale,
+                                               hipStream_t stream) {
+    if (!valid_dtype(h_dtype) || !valid_qtype(qtype)) return W8A8_ERR_INVALID_ARG;
+    if (!(eps >= 0.0f && eps < 1.0f)) return W8A8_ERR_INVALID_ARG;
+    if (M > 0 && (!h || !xq || !x_scale)) return W8A8_ERR_INVALID_ARG;
+    w8a8_status st = check_dims(M, 0, K);
+    if (st != W8A8_OK) return st;
+    if (K > 8192) return W8A8_ERR_UNSUPPORTED;            // rows are held in registers
+    if (M == 0) return W8A8_OK;
+    if (!aligned16(h) || !aligned16(g) || !aligned16(b) || !aligned16(xq) || !aligned16(x_scale))
+        return W8A8_ERR_UNSUPPORTED;
+    return from_hip(w8a8::launch_norm_quant_act(h, h_dtype == W8A8_BF16, M, K, g, b, true, eps,
+                                                qtype == W8A8_FP8_E4M3, static_cast<uint8_t*>(xq), x_scale, stream));
 }
 
 // ---- weight-only W8A16 ------------------------------------------------------------------------------

@@ -74,10 +74,11 @@ hipError_t launch_gemm(const uint8_t* xq, const float* x_scale, const uint8_t* w
                        bool fp8, bool tensor_scales, int64_t M, int64_t N, int64_t K, uint16_t* y, void* acc,
                        hipStream_t st);
 
-// RMS norm with gain g (g' = g / s folded in; NULL = 1) and the per-token quantize, one pass over
-// h [M, K] (K <= 8192): xq [M, K] codes and x_scale [M].
-hipError_t launch_norm_quant_act(const void* h, bool bf16, int64_t M, int64_t K, const float* g, float eps, bool fp8,
-                                 uint8_t* xq, float* x_scale, hipStream_t st);
+// RMS norm with gain g (g' = g / s folded in; NULL = 1), or with layer a LayerNorm with gain g and
+// bias b (NULL = 1 and 0), and the per-token quantize, one pass over h [M, K] (K <= 8192):
+// xq [M, K] codes and x_scale [M].
+hipError_t launch_norm_quant_act(const void* h, bool bf16, int64_t M, int64_t K, const float* g, const float* b,
+                                 bool layer, float eps, bool fp8, uint8_t* xq, float* x_scale, hipStream_t st);
 
 // out[j] = g[j] / s[j] (correctly rounded; NULL operands are 1).
 hipError_t launch_fold_norm_gain(const float* g, const float* s, int64_t K, float* out, hipStream_t st);

@@ -454,9 +454,21 @@ __device__ __forceinline__ float certified_mean(double sum, double inv_k) {
     return lo == hi ? lo : -1.0f;
 }
 
-// The row's mean square from the double-double sum of this lane's squares: a butterfly across the
-// wave, then (kSplit > 1) an exchange across the row's waves.  Called by every wave of the block.
-template <int kChunks, int kSplit>
+// The float mean of a signed sum estimate within 2^-47 of the sum of |terms| (abs_sum) from the
+// exact sum, into out; false when the band around it straddles a float rounding boundary.
+__device__ __forceinline__ bool certified_mean_signed(double sum, double abs_sum, double inv_k, float& out) {
+    const double q = sum * inv_k;
+    const double err = abs_sum * inv_k * 0x1p-44;
+    const float lo = static_cast<float>(q - err);
+    const float hi = static_cast<float>(q + err);
+    out = lo;
+    return lo == hi;
+}
+
+// The row's mean of v (kSquare: of v^2) from the double-double sum of this lane's terms: a
+// butterfly across the wave, then (kSplit > 1) an exchange across the row's waves.  Called by
+// every wave of the block.
+template <int kChunks, int kSplit, bool kSquare = true>
 __device__ __forceinline__ float dd_mean(const float (&v)[kChunks][8], int lane_c, int64_t nchunk, int64_t K,
                                          int lane, int wave, int slot, double (*xhi)[kActWaves],
                                          double (*xlo)[kActWaves], int buf) {
@@ -466,7 +478,9 @@ __device__ __forceinline__ float dd_mean(const float (&v)[kChunks][8], int lane_
     for (int i = 0; i < kChunks; ++i) {
         if (lane_c + static_cast<int64_t>(kStride) * i < nchunk) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) dd_add(hi, lo, static_cast<double>(v[i][e]) * static_cast<double>(v[i][e]));
+            for (int e = 0; e < 8; ++e)
+                dd_add(hi, lo, kSquare ? static_cast<double>(v[i][e]) * static_cast<double>(v[i][e])
+                                       : static_cast<double>(v[i][e]));
         }
     }
 #pragma unroll
@@ -488,21 +502,38 @@ __device__ __forceinline__ float dd_mean(const float (&v)[kChunks][8], int lane_
     return static_cast<float>((hi + lo) / static_cast<double>(K));
 }
 
-template <bool kBf16, bool kFp8, int kChunks, bool kGain, int kSplit>
+// Norm kinds: RMS norm without or with a gain, and LayerNorm (gain g' and bias b', staged as 1
+// and 0 where not given).
+constexpr int kRmsNorm = 0, kRmsNormGain = 1, kLayerNorm = 2;
+
+// LayerNorm ("Weight-Activation Quantization", s3 step 1 with the norm before the layer a
+// LayerNorm: 1/s folded into both gain and bias): mu = the float mean of the exact sum of h, d =
+// h - mu in fp32, var = the float mean of the exact sum of d^2, r = 1 / sqrt(var + eps), X~ =
+// (d * r) * g' + b' rounded after each operation.  The mean's sum has signed terms, so its plain
+// double estimate is certified against a band of 2^-44 of the sum of |h| (the error bound of the
+// 41 additions is 41 * 2^-53 of it), with the same double-double fallback.
+template <bool kBf16, bool kFp8, int kChunks, int kMode, int kSplit>
 __global__ __launch_bounds__(kActWaves * kWave) void norm_quant_kernel(
-    const void* __restrict__ h, const float* __restrict__ g, float eps, int64_t M, int64_t K, int rows_per_wave,
-    uint8_t* __restrict__ q, float* __restrict__ scale) {
-    extern __shared__ float sh_g[];             // kGain: g', K floats (lds_half order)
+    const void* __restrict__ h, const float* __restrict__ g, const float* __restrict__ b, float eps, int64_t M,
+    int64_t K, int rows_per_wave, uint8_t* __restrict__ q, float* __restrict__ scale) {
+    constexpr bool kGain = kMode != kRmsNorm, kLayer = kMode == kLayerNorm;
+    extern __shared__ float sh_g[];             // kGain: g', K floats; kLayer: then b', K floats (lds_half order)
     __shared__ double xsum[2][kActWaves], xhi[2][kActWaves], xlo[2][kActWaves];
+    __shared__ double xmsum[2][kActWaves], xmabs[2][kActWaves], xmhi[2][kActWaves], xmlo[2][kActWaves];
     __shared__ float xmax[2][kActWaves];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int64_t nchunk = K / 8;
+    float* const sh_b = sh_g + K;
     if constexpr (kGain) {
         constexpr int kPer = kSplit * kChunks;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int64_t j = threadIdx.x + static_cast<int64_t>(i) * blockDim.x;
-            if (j < K) sh_g[lds_half(j, nchunk)] = g[j];
+            if (j < K) {
+                const int hj = lds_half(j, nchunk);
+                sh_g[hj] = (!kLayer || g) ? g[j] : 1.0f;
+                if constexpr (kLayer) sh_b[hj] = b ? b[j] : 0.0f;
+            }
         }
         __syncthreads();
     }
@@ -526,6 +557,58 @@ __global__ __launch_bounds__(kActWaves * kWave) void norm_quant_kernel(
         float v[kChunks][8];
 #pragma unroll
         for (int i = 0; i < kChunks; ++i) unpack8<kBf16>(raw[i], v[i]);
+        const double inv_k = 1.0 / static_cast<double>(K);
+        if constexpr (kLayer) {
+            // The mean, then v becomes d = v - mu (fp32).
+            double msum = 0.0, mabs = 0.0;
+#pragma unroll
+            for (int i = 0; i < kChunks; ++i) {
+                if (lane_c + static_cast<int64_t>(kStride) * i < nchunk) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const double d = static_cast<double>(v[i][e]);
+                        msum += d;
+                        mabs += __builtin_fabs(d);
+                    }
+                }
+            }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                msum += __shfl_xor(msum, off, kWave);
+                mabs += __shfl_xor(mabs, off, kWave);
+            }
+            float mu;
+            if constexpr (kSplit == 1) {
+                if (!certified_mean_signed(msum, mabs, inv_k, mu))
+                    mu = dd_mean<kChunks, 1, false>(v, lane_c, nchunk, K, lane, wave, slot, xmhi, xmlo, rr & 1);
+            } else {
+                if (lane == 0) {
+                    xmsum[rr & 1][wave] = msum;
+                    xmabs[rr & 1][wave] = mabs;
+                }
+                __syncthreads();
+                bool straddle = false;
+                mu = 0.0f;
+#pragma unroll
+                for (int t = 0; t < kRowsPerPass; ++t) {
+                    double st = xmsum[rr & 1][t * kSplit], sa = xmabs[rr & 1][t * kSplit];
+#pragma unroll
+                    for (int p = 1; p < kSplit; ++p) {
+                        st += xmsum[rr & 1][t * kSplit + p];
+                        sa += xmabs[rr & 1][t * kSplit + p];
+                    }
+                    float mt;
+                    straddle |= !certified_mean_signed(st, sa, inv_k, mt);
+                    if (t == slot) mu = mt;
+                }
+                if (straddle)
+                    mu = dd_mean<kChunks, kSplit, false>(v, lane_c, nchunk, K, lane, wave, slot, xmhi, xmlo, rr & 1);
+            }
+#pragma unroll
+            for (int i = 0; i < kChunks; ++i)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[i][e] = __fsub_rn(v[i][e], mu);
+        }
         // Sum of squares over this lane's chunks (re-read chunks past the row end do not count): a
         // plain double sum of exact squares, the same in every lane after the xor butterfly.
         double sum = 0.0;
@@ -541,7 +624,6 @@ __global__ __launch_bounds__(kActWaves * kWave) void norm_quant_kernel(
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, kWave);
-        const double inv_k = 1.0 / static_cast<double>(K);
         float ms;
         if constexpr (kSplit == 1) {
             ms = certified_mean(sum, inv_k);
@@ -577,10 +659,25 @@ __global__ __launch_bounds__(kActWaves * kWave) void norm_quant_kernel(
                 gv[0] = g0.x; gv[1] = g0.y; gv[2] = g0.z; gv[3] = g0.w;
                 gv[4] = g1.x; gv[5] = g1.y; gv[6] = g1.z; gv[7] = g1.w;
             }
+            if constexpr (kLayer) {
+                const float4 b0 = *reinterpret_cast<const float4*>(sh_b + c * 4);
+                const float4 b1 = *reinterpret_cast<const float4*>(sh_b + (nchunk + c) * 4);
+                const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                v[i][e] = (v[i][e] * r) * gv[e];
-                amax = fmaxf(amax, fabsf(v[i][e]));
+                for (int e = 0; e < 8; ++e) {
+                    // Each operation rounded on its own: the compiler must not fuse the multiply
+                    // and the add.
+#pragma clang fp contract(off)
+                    const float t = (v[i][e] * r) * gv[e];
+                    v[i][e] = t + bv[e];
+                    amax = fmaxf(amax, fabsf(v[i][e]));
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    v[i][e] = (v[i][e] * r) * gv[e];
+                    amax = fmaxf(amax, fabsf(v[i][e]));
+                }
             }
         }
         amax = wave_max(amax);
@@ -609,30 +706,33 @@ __global__ __launch_bounds__(kActWaves * kWave) void norm_quant_kernel(
 }
 
 template <bool kBf16, bool kFp8, int kChunks, int kSplit>
-void norm_quant_launch(const void* h, const float* g, float eps, int64_t M, int64_t K, uint8_t* xq, float* xs,
-                       hipStream_t st) {
+void norm_quant_launch(const void* h, const float* g, const float* b, bool layer, float eps, int64_t M, int64_t K,
+                       uint8_t* xq, float* xs, hipStream_t st) {
     const int64_t rows_per_pass = kActWaves / kSplit;
     const int64_t rows_per_block_pass = rows_per_pass * 512;
     const int rpw = static_cast<int>(std::max<int64_t>(1, (M + rows_per_block_pass - 1) / rows_per_block_pass));
     const int64_t rows_per_block = rows_per_pass * rpw;
     dim3 grid(static_cast<unsigned>((M + rows_per_block - 1) / rows_per_block)), block(kActWaves * kWave);
-    if (g)
-        hipLaunchKernelGGL((norm_quant_kernel<kBf16, kFp8, kChunks, true, kSplit>), grid, block,
-                           static_cast<size_t>(K) * sizeof(float), st, h, g, eps, M, K, rpw, xq, xs);
+    if (layer)
+        hipLaunchKernelGGL((norm_quant_kernel<kBf16, kFp8, kChunks, kLayerNorm, kSplit>), grid, block,
+                           2 * static_cast<size_t>(K) * sizeof(float), st, h, g, b, eps, M, K, rpw, xq, xs);
+    else if (g)
+        hipLaunchKernelGGL((norm_quant_kernel<kBf16, kFp8, kChunks, kRmsNormGain, kSplit>), grid, block,
+                           static_cast<size_t>(K) * sizeof(float), st, h, g, b, eps, M, K, rpw, xq, xs);
     else
-        hipLaunchKernelGGL((norm_quant_kernel<kBf16, kFp8, kChunks, false, kSplit>), grid, block, 0, st, h, g, eps, M,
-                           K, rpw, xq, xs);
+        hipLaunchKernelGGL((norm_quant_kernel<kBf16, kFp8, kChunks, kRmsNorm, kSplit>), grid, block, 0, st, h, g, b,
+                           eps, M, K, rpw, xq, xs);
 }
 
 template <bool kBf16, bool kFp8>
-hipError_t norm_quant_dispatch(const void* h, const float* g, float eps, int64_t M, int64_t K, uint8_t* xq, float* xs,
-                               hipStream_t st) {
+hipError_t norm_quant_dispatch(const void* h, const float* g, const float* b, bool layer, float eps, int64_t M,
+                               int64_t K, uint8_t* xq, float* xs, hipStream_t st) {
     const int64_t per_lane = (K / 8 + kWave - 1) / kWave;
-    if (per_lane <= 1) norm_quant_launch<kBf16, kFp8, 1, 1>(h, g, eps, M, K, xq, xs, st);
-    else if (per_lane <= 2) norm_quant_launch<kBf16, kFp8, 2, 1>(h, g, eps, M, K, xq, xs, st);
-    else if (per_lane <= 4) norm_quant_launch<kBf16, kFp8, 4, 1>(h, g, eps, M, K, xq, xs, st);
-    else if (per_lane <= 8) norm_quant_launch<kBf16, kFp8, 4, 2>(h, g, eps, M, K, xq, xs, st);
-    else if (per_lane <= 16) norm_quant_launch<kBf16, kFp8, 4, 4>(h, g, eps, M, K, xq, xs, st);
+    if (per_lane <= 1) norm_quant_launch<kBf16, kFp8, 1, 1>(h, g, b, layer, eps, M, K, xq, xs, st);
+    else if (per_lane <= 2) norm_quant_launch<kBf16, kFp8, 2, 1>(h, g, b, layer, eps, M, K, xq, xs, st);
+    else if (per_lane <= 4) norm_quant_launch<kBf16, kFp8, 4, 1>(h, g, b, layer, eps, M, K, xq, xs, st);
+    else if (per_lane <= 8) norm_quant_launch<kBf16, kFp8, 4, 2>(h, g, b, layer, eps, M, K, xq, xs, st);
+    else if (per_lane <= 16) norm_quant_launch<kBf16, kFp8, 4, 4>(h, g, b, layer, eps, M, K, xq, xs, st);
     else return hipErrorInvalidValue;       // K > 8192: refused by the C ABI before this point
     return hipGetLastError();
 }
@@ -813,13 +913,13 @@ hipError_t launch_quant_act(const void* x, bool bf16, int64_t M, int64_t K, cons
                : quant_act_dispatch<false, false>(x, M, K, s, xq, x_scale, st);
 }
 
-hipError_t launch_norm_quant_act(const void* h, bool bf16, int64_t M, int64_t K, const float* g, float eps, bool fp8,
-                                 uint8_t* xq, float* x_scale, hipStream_t st) {
+hipError_t launch_norm_quant_act(const void* h, bool bf16, int64_t M, int64_t K, const float* g, const float* b,
+                                 bool layer, float eps, bool fp8, uint8_t* xq, float* x_scale, hipStream_t st) {
     if (M <= 0) return hipSuccess;
-    if (bf16) return fp8 ? norm_quant_dispatch<true, true>(h, g, eps, M, K, xq, x_scale, st)
-                         : norm_quant_dispatch<true, false>(h, g, eps, M, K, xq, x_scale, st);
-    return fp8 ? norm_quant_dispatch<false, true>(h, g, eps, M, K, xq, x_scale, st)
-               : norm_quant_dispatch<false, false>(h, g, eps, M, K, xq, x_scale, st);
+    if (bf16) return fp8 ? norm_quant_dispatch<true, true>(h, g, b, layer, eps, M, K, xq, x_scale, st)
+                         : norm_quant_dispatch<true, false>(h, g, b, layer, eps, M, K, xq, x_scale, st);
+    return fp8 ? norm_quant_dispatch<false, true>(h, g, b, layer, eps, M, K, xq, x_scale, st)
+               : norm_quant_dispatch<false, false>(h, g, b, layer, eps, M, K, xq, x_scale, st);
 }
 
 hipError_t launch_fold_norm_gain(const float* g, const float* s, int64_t K, float* out, hipStream_t st) {

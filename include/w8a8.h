@@ -192,8 +192,9 @@ w8a8_status w8a8_gemm_dequant_tensor(const void* xq, const float* x_scale, const
 /*
  * ---- The smoothing folded into the layer before ([WAQ] s3 step 1: the SmoothQuant transform is
  * done offline, during model preparation; the W8A16-vs-W8A8 lesson, s2: no runtime overhead).
- * The activations X come from an RMS norm of the residual stream h with gain g; 1/s is folded into
- * that gain once, and the norm, the smoothing and the per-token quantize run as one pass over h.
+ * The activations X come from an RMS norm (or a LayerNorm) of the residual stream h with gain g
+ * (and bias b); 1/s is folded into them once, and the norm, the smoothing and the per-token
+ * quantize run as one pass over h.
  */
 
 /* g_out[j] = g[j] / s[j] (fp32, correctly rounded); g or s NULL count as 1.  K >= 1. */
@@ -210,6 +211,21 @@ w8a8_status w8a8_fold_norm_gain(const float* g, const float* s, int64_t K, float
  */
 w8a8_status w8a8_norm_quant_act(const void* h, w8a8_dtype h_dtype, int64_t M, int64_t K, const float* g,
                                 float eps, w8a8_qtype qtype, void* xq, float* x_scale, hipStream_t stream);
+
+/*
+ * The same with a LayerNorm before the layer ([WAQ] s3 step 1; 1/s is folded into both its gain
+ * and its bias, b'[j] = b[j] / s[j], by w8a8_fold_norm_gain(b, s, ...)).  Per row i of h:
+ *   mu       = (float)(sum_j (double)h[i, j] / K)     (the sum exact to about 2^-100: order-free)
+ *   d[j]     = h[i, j] - mu                           (fp32)
+ *   var      = (float)(sum_j (double)d[j]^2 / K)      (likewise)
+ *   r        = 1 / sqrt(var + eps)
+ *   X~[i, j] = (d[j] * r) * g[j] + b[j]               (fp32, rounded after each operation, no fused
+ *                                                      multiply-add; g NULL: 1, b NULL: 0)
+ * then x_scale[i] and xq[i, :] as w8a8_norm_quant_act.  Arguments, limits and errors as there.
+ */
+w8a8_status w8a8_layer_norm_quant_act(const void* h, w8a8_dtype h_dtype, int64_t M, int64_t K, const float* g,
+                                      const float* b, float eps, w8a8_qtype qtype, void* xq, float* x_scale,
+                                      hipStream_t stream);
 
 /*
  * ---- Weight-only W8A16, the contrast the pages draw with W8A8 ([WAQ] s1 "Why Quantize Activations

@@ -118,6 +118,14 @@ def test_argument_validation_without_gpu():
     assert L.w8a8_norm_quant_act(fake, 1, 4, 8208, None, 1e-5, 0, fake, fake, None) == UNS  # K > 8192
     assert L.w8a8_norm_quant_act(None, 1, 0, 16, None, 1e-5, 0, None, None, None) == OK     # M = 0
     assert L.w8a8_fold_norm_gain(None, None, 0, fake, None) == INV                          # K = 0
+    L.w8a8_layer_norm_quant_act.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_int,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert L.w8a8_layer_norm_quant_act(fake, 1, 4, 16, None, None, -1.0, 0, fake, fake, None) == INV   # eps < 0
+    assert L.w8a8_layer_norm_quant_act(fake, 1, 4, 16, None, None, 1e-5, 2, fake, fake, None) == INV   # bad qtype
+    assert L.w8a8_layer_norm_quant_act(fake, 1, 4, 8208, None, None, 1e-5, 0, fake, fake, None) == UNS  # K > 8192
+    assert L.w8a8_layer_norm_quant_act(fake, 1, 4, 16, None, odd, 1e-5, 0, fake, fake, None) == UNS    # bias alignment
+    assert L.w8a8_layer_norm_quant_act(None, 1, 0, 16, None, None, 1e-5, 0, None, None, None) == OK   # M = 0
 
 
 def test_product_path_does_not_touch_the_oracle():

@@ -125,3 +125,100 @@ def test_norm_quant_act_prefill_shape(f):
     q_ref, sx_ref = oracle.norm_quant_act(X, gf_h, 1e-5, "int8")
     np.testing.assert_array_equal(host(sx), sx_ref)
     np.testing.assert_array_equal(host(xq), q_ref)
+
+
+# ---- LayerNorm with the smoothing folded into gain and bias ----------------------------------
+
+@pytest.mark.parametrize("qtype", ["int8", "fp8"])
+@pytest.mark.parametrize("M,K", SHAPES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_layer_norm_quant_act(f, qtype, M, K, dtype):
+    """Rows with a nonzero mean (an offset of 3 on top of the outlier-channel draw)."""
+    announce(f"layer_norm_quant_act {qtype} {dtype} {M}x{K}")
+    H = synth.random_matrix((M, K), seed=M * 17 + K, outliers=max(1, K // 100)) + np.float32(3.0)
+    if dtype == "bf16":
+        H = synth.f32_to_bf16_bits(H)
+    gf = folded_gain(f, K, seed=K + 1)
+    b = synth.random_scales(K, seed=K + 2, lo=-1.0, hi=1.0)
+    s = synth.random_scales(K, seed=K + 3, lo=0.05, hi=20.0)
+    bf = f.w8a8_fold_norm_gain(dev(b), dev(s))
+    torch.cuda.synchronize()
+    bf = host(bf)
+    np.testing.assert_array_equal(bf, oracle.fold_norm_gain(b, s))
+    for g, bb, eps in ((gf, bf, 1e-5), (None, None, 1e-6), (gf, None, 0.0)):
+        xq, sx = f.w8a8_layer_norm_quant_act(dev(H), None if g is None else dev(g), None if bb is None else dev(bb),
+                                             eps, qtype)
+        torch.cuda.synchronize()
+        q_ref, sx_ref = oracle.layer_norm_quant_act(H, g, bb, eps, qtype)
+        np.testing.assert_array_equal(host(sx), sx_ref)
+        np.testing.assert_array_equal(codes(host(xq)), codes(q_ref))
+
+
+@pytest.mark.parametrize("qtype", ["int8", "fp8"])
+def test_layer_norm_wide_range_constant_and_zero_rows(f, qtype):
+    """Rows spanning 2^40 (d = h - mu not exact in fp32), a constant row (d = 0: X~ = b), an
+    all-zero row, and eps = 0 for the rows that allow it."""
+    announce(f"layer_norm_quant_act wide range {qtype}")
+    rng = np.random.Generator(np.random.PCG64(81))
+    H = rng.standard_normal((48, 4096)).astype(np.float32)
+    H *= np.exp2(rng.integers(-20, 20, H.shape)).astype(np.float32)
+    H[5] = 0.0
+    H[9] = np.float32(-2.75)
+    g = synth.random_scales(4096, seed=82, lo=0.5, hi=2.0)
+    b = synth.random_scales(4096, seed=83, lo=-1.0, hi=1.0)
+    xq, sx = f.w8a8_layer_norm_quant_act(dev(H), dev(g), dev(b), 1e-5, qtype)
+    torch.cuda.synchronize()
+    q_ref, sx_ref = oracle.layer_norm_quant_act(H, g, b, 1e-5, qtype)
+    np.testing.assert_array_equal(host(sx), sx_ref)
+    np.testing.assert_array_equal(codes(host(xq)), codes(q_ref))
+    Hn = np.delete(H, [5, 9], axis=0)
+    xq, sx = f.w8a8_layer_norm_quant_act(dev(Hn), dev(g), None, 0.0, qtype)
+    torch.cuda.synchronize()
+    q_ref, sx_ref = oracle.layer_norm_quant_act(Hn, g, None, 0.0, qtype)
+    np.testing.assert_array_equal(host(sx), sx_ref)
+    np.testing.assert_array_equal(codes(host(xq)), codes(q_ref))
+
+
+@pytest.mark.parametrize("qtype", ["int8", "fp8"])
+@pytest.mark.parametrize("K", [128, 1024, 2048, 4096, 8192])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_layer_norm_mean_and_variance_ties(f, qtype, K, dtype):
+    """Rows whose mean, or whose variance, sits on a float rounding tie or just past it by terms a
+    plain double sum drops, among random rows in several passes of a block.  With the gain
+    g[0] = 2^-20 the entries at the mean set the scale, so a mean taken from a plain sum changes
+    the scales of the mean pairs; the variance pairs normalize differently at eps = 0."""
+    announce(f"layer_norm mean/variance ties {qtype} {dtype} K={K}")
+    M = 41
+    H = synth.random_matrix((M, K), seed=K + 9, outliers=max(1, K // 100))
+    for r0 in (0, 7, 22):
+        H[r0:r0 + 2] = synth.mean_tie_rows(K)
+    for r0 in (3, 17, 39):
+        H[r0:r0 + 2] = synth.variance_tie_rows(K)
+    if dtype == "bf16":
+        H = synth.f32_to_bf16_bits(H)
+    g = np.ones(K, np.float32)
+    g[0] = 2.0 ** -20
+    for gg, eps in ((g, 0.0), (None, 0.0), (g, 1e-5)):
+        xq, sx = f.w8a8_layer_norm_quant_act(dev(H), None if gg is None else dev(gg), None, eps, qtype)
+        torch.cuda.synchronize()
+        q_ref, sx_ref = oracle.layer_norm_quant_act(H, gg, None, eps, qtype)
+        np.testing.assert_array_equal(host(sx), sx_ref)
+        np.testing.assert_array_equal(codes(host(xq)), codes(q_ref))
+        if gg is not None and eps == 0.0:
+            assert sx_ref[0] != sx_ref[1]
+
+
+def test_layer_norm_prefill_shape(f):
+    """The prefill workload's activations read as the residual stream, gain and bias folded."""
+    announce("layer_norm_quant_act prefill shape")
+    X, W = synth.make_inputs("c2")
+    x, w = dev(X), dev(W)
+    _, _, s = f.w8a8_smooth_scales(x, w, 0.5)
+    g = synth.random_scales(X.shape[1], seed=84, lo=0.5, hi=2.0)
+    b = synth.random_scales(X.shape[1], seed=85, lo=-0.5, hi=0.5)
+    gf, bf = f.w8a8_fold_norm_gain(dev(g), s), f.w8a8_fold_norm_gain(dev(b), s)
+    xq, sx = f.w8a8_layer_norm_quant_act(x, gf, bf, 1e-5, "int8")
+    torch.cuda.synchronize()
+    q_ref, sx_ref = oracle.layer_norm_quant_act(X, host(gf), host(bf), 1e-5, "int8")
+    np.testing.assert_array_equal(host(sx), sx_ref)
+    np.testing.assert_array_equal(host(xq), q_ref)
