@@ -116,30 +116,24 @@ __device__ __forceinline__ int int8_code(float q) {
     return static_cast<int>(r);
 }
 
-// OCP E4M3 ("fn") code of q, |q| <= 448 (callers clamp first), round to nearest even.
-// Normal range (|q| >= 2^-6): keep 3 of the 23 fp32 mantissa bits with round-half-even on the
-// bit pattern (a carry moves into the exponent, which is the correct result), then rebias the
-// exponent from 127 to 7.  Below 2^-6 the E4M3 spacing is 2^-9, so the code is rint(|q| * 2^9)
-// (0..8, where 8 is the smallest normal, 2^-6, whose code is also 8).
-__device__ __forceinline__ uint32_t e4m3_code(float q) {
-    uint32_t u = __float_as_uint(q);
-    uint32_t sign = (u >> 24) & 0x80u;
-    uint32_t a = u & 0x7FFFFFFFu;
-    uint32_t mag;
-    if (a >= 0x3C800000u) {
-        uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
-        mag = r - (120u << 3);
-    } else {
-        mag = static_cast<uint32_t>(__builtin_rintf(__uint_as_float(a) * 512.0f));
-    }
-    return sign | mag;
+// Two OCP E4M3 ("fn": bias 7, largest 448, subnormals m * 2^-9) codes from the conversion
+// instruction v_cvt_pk_fp8_f32, which on gfx950 rounds to the nearest E4M3 value with ties to
+// even and keeps the sign of zero.  q0 goes to byte 2 kHi and q1 to byte 2 kHi + 1 of old, whose
+// other two bytes are kept.  Inputs are clamped to +-448 first, so nothing overflows.  An in-bounds
+// probe matched torch's float8_e4m3fn cast on every representable value, every midpoint between
+// two of them, the neighbouring floats of both, subnormals and signed zeros.
+template <bool kHi>
+__device__ __forceinline__ uint32_t e4m3_pair(float q0, float q1, uint32_t old) {
+    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(q0, -448.0f), 448.0f),
+                                                                 fminf(fmaxf(q1, -448.0f), 448.0f),
+                                                                 static_cast<int>(old), kHi));
 }
 
 // Code of a quotient q = v / scale (already divided).
 template <bool kFp8>
 __device__ __forceinline__ uint32_t code_of_q(float q) {
     if constexpr (kFp8) {
-        return e4m3_code(fminf(fmaxf(q, -448.0f), 448.0f));
+        return e4m3_pair<false>(q, 0.0f, 0u) & 0xFFu;
     } else {
         return static_cast<uint32_t>(int8_code(q)) & 0xFFu;
     }
@@ -158,8 +152,7 @@ __device__ __forceinline__ uint32_t code_of(float xs, float scale) {
 template <bool kFp8>
 __device__ __forceinline__ uint32_t pack_codes4(float q0, float q1, float q2, float q3) {
     if constexpr (kFp8) {
-        return code_of_q<true>(q0) | (code_of_q<true>(q1) << 8) | (code_of_q<true>(q2) << 16) |
-               (code_of_q<true>(q3) << 24);
+        return e4m3_pair<true>(q2, q3, e4m3_pair<false>(q0, q1, 0u));
     } else {
         auto rounded = [](float q) { return __float_as_uint(fminf(fmaxf(q, -127.0f), 127.0f) + 12582912.0f); };
         // v_perm_b32 selectors: 0-3 pick bytes of the second operand, 4-7 of the first, 0x0c gives 0.
