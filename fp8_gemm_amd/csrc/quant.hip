@@ -454,9 +454,18 @@ __device__ __forceinline__ float certified_mean(double sum, double inv_k) {
     return lo == hi ? lo : -1.0f;
 }
 
-// The float mean of a signed sum estimate within 2^-47 of the sum of |terms| (abs_sum) from the
-// exact sum, into out; false when the band around it straddles a float rounding boundary.
-__device__ __forceinline__ bool certified_mean_signed(double sum, double abs_sum, double inv_k, float& out) {
+// The float mean of a signed sum of K terms, into out; false when it cannot be certified.  When
+// every term is a multiple of 2^qexp and abs_sum <= 2^(52 + qexp) (a factor 2 of margin over 2^53
+// for the rounding of abs_sum itself), every partial sum is exact in double, so sum is the exact
+// sum and the correctly rounded sum / K is the value the exact mean rounds to (inputs with few
+// significant bits, as bf16, often land exactly on a float tie, and this decides it).  Otherwise
+// the estimate is within 2^-47 of abs_sum from the exact sum and the band test applies.
+__device__ __forceinline__ bool certified_mean_signed(double sum, double abs_sum, int qexp, int64_t K, float& out) {
+    if (abs_sum <= __builtin_ldexp(1.0, 52 + qexp)) {
+        out = static_cast<float>(sum / static_cast<double>(K));
+        return true;
+    }
+    const double inv_k = 1.0 / static_cast<double>(K);
     const double q = sum * inv_k;
     const double err = abs_sum * inv_k * 0x1p-44;
     const float lo = static_cast<float>(q - err);
@@ -509,9 +518,10 @@ constexpr int kRmsNorm = 0, kRmsNormGain = 1, kLayerNorm = 2;
 // LayerNorm ("Weight-Activation Quantization", s3 step 1 with the norm before the layer a
 // LayerNorm: 1/s folded into both gain and bias): mu = the float mean of the exact sum of h, d =
 // h - mu in fp32, var = the float mean of the exact sum of d^2, r = 1 / sqrt(var + eps), X~ =
-// (d * r) * g' + b' rounded after each operation.  The mean's sum has signed terms, so its plain
-// double estimate is certified against a band of 2^-44 of the sum of |h| (the error bound of the
-// 41 additions is 41 * 2^-53 of it), with the same double-double fallback.
+// (d * r) * g' + b' rounded after each operation.  The mean's sum has signed terms: its plain
+// double estimate is exact when the row's values are multiples of a quantum small enough, and is
+// otherwise certified against a band of 2^-44 of the sum of |h| (the error bound of the 41
+// additions is 41 * 2^-53 of it), with the same double-double fallback.
 template <bool kBf16, bool kFp8, int kChunks, int kMode, int kSplit>
 __global__ __launch_bounds__(kActWaves * kWave) void norm_quant_kernel(
     const void* __restrict__ h, const float* __restrict__ g, const float* __restrict__ b, float eps, int64_t M,
@@ -520,6 +530,7 @@ __global__ __launch_bounds__(kActWaves * kWave) void norm_quant_kernel(
     extern __shared__ float sh_g[];             // kGain: g', K floats; kLayer: then b', K floats (lds_half order)
     __shared__ double xsum[2][kActWaves], xhi[2][kActWaves], xlo[2][kActWaves];
     __shared__ double xmsum[2][kActWaves], xmabs[2][kActWaves], xmhi[2][kActWaves], xmlo[2][kActWaves];
+    __shared__ int xmexp[2][kActWaves];
     __shared__ float xmax[2][kActWaves];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int64_t nchunk = K / 8;
@@ -560,7 +571,11 @@ __global__ __launch_bounds__(kActWaves * kWave) void norm_quant_kernel(
         const double inv_k = 1.0 / static_cast<double>(K);
         if constexpr (kLayer) {
             // The mean, then v becomes d = v - mu (fp32).
+            // Sum, sum of |h| and the smallest exponent of a nonzero h (frexp: |h| = m 2^e, m in
+            // [1/2, 1)); a nonzero input is then a multiple of 2^(e - kMant).
+            constexpr int kMant = kBf16 ? 8 : 24;
             double msum = 0.0, mabs = 0.0;
+            int mexp = 1 << 20;
 #pragma unroll
             for (int i = 0; i < kChunks; ++i) {
                 if (lane_c + static_cast<int64_t>(kStride) * i < nchunk) {
@@ -569,6 +584,7 @@ __global__ __launch_bounds__(kActWaves * kWave) void norm_quant_kernel(
                         const double d = static_cast<double>(v[i][e]);
                         msum += d;
                         mabs += __builtin_fabs(d);
+                        mexp = min(mexp, v[i][e] != 0.0f ? __builtin_amdgcn_frexp_expf(v[i][e]) : (1 << 20));
                     }
                 }
             }
@@ -576,15 +592,17 @@ __global__ __launch_bounds__(kActWaves * kWave) void norm_quant_kernel(
             for (int off = 32; off >= 1; off >>= 1) {
                 msum += __shfl_xor(msum, off, kWave);
                 mabs += __shfl_xor(mabs, off, kWave);
+                mexp = min(mexp, __shfl_xor(mexp, off, kWave));
             }
             float mu;
             if constexpr (kSplit == 1) {
-                if (!certified_mean_signed(msum, mabs, inv_k, mu))
+                if (!certified_mean_signed(msum, mabs, mexp - kMant, K, mu))
                     mu = dd_mean<kChunks, 1, false>(v, lane_c, nchunk, K, lane, wave, slot, xmhi, xmlo, rr & 1);
             } else {
                 if (lane == 0) {
                     xmsum[rr & 1][wave] = msum;
                     xmabs[rr & 1][wave] = mabs;
+                    xmexp[rr & 1][wave] = mexp;
                 }
                 __syncthreads();
                 bool straddle = false;
@@ -592,13 +610,15 @@ __global__ __launch_bounds__(kActWaves * kWave) void norm_quant_kernel(
 #pragma unroll
                 for (int t = 0; t < kRowsPerPass; ++t) {
                     double st = xmsum[rr & 1][t * kSplit], sa = xmabs[rr & 1][t * kSplit];
+                    int se = xmexp[rr & 1][t * kSplit];
 #pragma unroll
                     for (int p = 1; p < kSplit; ++p) {
                         st += xmsum[rr & 1][t * kSplit + p];
                         sa += xmabs[rr & 1][t * kSplit + p];
+                        se = min(se, xmexp[rr & 1][t * kSplit + p]);
                     }
                     float mt;
-                    straddle |= !certified_mean_signed(st, sa, inv_k, mt);
+                    straddle |= !certified_mean_signed(st, sa, se - kMant, K, mt);
                     if (t == slot) mu = mt;
                 }
                 if (straddle)
