@@ -137,3 +137,13 @@ def test_smooth_quant_empty(f, M, N):
         qx, sx = oracle.quant_act(X, s, "int8")
         np.testing.assert_array_equal(host(r["x_scale"]), sx)
         np.testing.assert_array_equal(codes(host(r["xq"])), codes(qx))
+
+
+@pytest.mark.parametrize("name", ["c3", "c5"])
+def test_smooth_quant_large_workloads(f, name):
+    """The MLP-up (INT8) and large FP8 workloads at full size, as the benchmark step runs them:
+    maxima, s, weight codes and scales, activation codes and scales bit-exact."""
+    wl = synth.workload(name)
+    announce(f"smooth_quant {wl.name}")
+    X, W = synth.make_inputs(wl, seed=0)
+    check(f, X, W, wl.alpha, wl.qtype)
