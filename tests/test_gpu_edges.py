@@ -406,3 +406,26 @@ def test_fp8_accumulators_within_bound(f):
         err = np.abs(acc - exact)
         assert np.all(err <= fp8_accumulation_bound(K, mag))
         assert np.linalg.norm(acc - exact) / np.linalg.norm(exact) < 1e-3
+
+
+@pytest.mark.parametrize("M", [5, 40, 300])
+def test_int8_largest_k(f, M):
+    """The largest K the INT8 path accepts (K * 127^2 < 2^31; the largest multiple of 16 is
+    133136): rows and columns of +-127 reach accumulators of +-2147350544, one short of overflow;
+    accumulators bit-exact and the dequantized output bit-exact against the oracle's fp32 one."""
+    announce(f"int8 largest K M={M}")
+    K, N = 133136, 48
+    assert K * 127 * 127 < 2 ** 31 and (K + 16) * 127 * 127 >= 2 ** 31
+    a = synth.random_codes((M, K), 81)
+    b = synth.random_codes((N, K), 82)
+    a[0], a[1], b[0], b[1] = 127, -127, 127, -127
+    xa, wb = dev(a), dev(b)
+    acc = host(f.w8a8_gemm_i32(xa, wb))
+    ref = oracle.gemm_i32(a, b)
+    np.testing.assert_array_equal(acc, ref)
+    assert acc[0, 0] == K * 127 * 127 and acc[1, 0] == -K * 127 * 127
+    sx = synth.random_scales(M, seed=83)
+    sw = synth.random_scales(N, seed=84)
+    y = host(f.w8a8_gemm_dequant(xa, dev(sx), wb, dev(sw), "int8"))
+    _, yb = oracle.dequant_i32(ref, sx, sw)
+    np.testing.assert_array_equal(y, yb)
