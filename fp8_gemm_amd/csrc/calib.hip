@@ -214,23 +214,23 @@ __global__ void smooth_factors_kernel(const float* __restrict__ ax, const float*
 }
 
 // Maximum of |a| over a whole tensor of nchunk 16-byte chunks (8 elements each), divided by
-// divisor when it is not 0.  Each thread keeps 8 chunks in flight per step of a grid-stride loop
-// (chunks past the end re-read the last one); the block's maximum is merged into out[0] with an
-// atomic maximum, skipped when out[0] already holds at least as much (out[0] only grows, so a
-// stale read can only cause a redundant atomic, never a missed one).
+// divisor when it is not 0.  Block b streams its own contiguous range of chunks, 8 chunks in
+// flight per thread (chunks past the range re-read its last one).  The block's maximum is merged
+// into out[0] with an atomic maximum, skipped when out[0] already holds at least as much (out[0]
+// only grows, so a stale read can only cause a redundant atomic, never a missed one).
 template <bool kBf16>
 __global__ __launch_bounds__(256) void absmax_tensor_kernel(const void* __restrict__ a, int64_t nchunk, float divisor,
                                                             float* __restrict__ out) {
     __shared__ float part[4];
     constexpr int kU = 8;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    const int64_t lo = block_range_lo(nchunk), hi = block_range_hi(nchunk);
     float m = 0.0f;
-    for (int64_t c0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c0 < nchunk; c0 += kU * stride) {
+    for (int64_t c0 = lo + threadIdx.x; c0 < hi; c0 += kU * blockDim.x) {
         float v[kU][8];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const int64_t c = c0 + u * stride;
-            load8<kBf16>(a, (c < nchunk ? c : nchunk - 1) * 8, v[u]);
+            const int64_t c = c0 + u * blockDim.x;
+            load8<kBf16>(a, (c < hi ? c : hi - 1) * 8, v[u]);
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u)

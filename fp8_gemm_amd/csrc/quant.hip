@@ -844,8 +844,8 @@ hipError_t quant_weight_dispatch(const void* w, int64_t K, int64_t N, const floa
 // ---- per-tensor quantize ("Weight-Activation Quantization", s4 "Per-Tensor Scaling for FP8") ----
 //
 // One scale for the whole tensor, scale = amax_in[0] / Q, so the kernel is a plain stream of
-// 16-byte chunks: 8 elements in, 8 codes out, kU chunks in flight per thread of a grid-stride
-// loop.  Under delayed scaling amax_in is an earlier tensor's maximum and values beyond Q * scale
+// 16-byte chunks: 8 elements in, 8 codes out.  Block b streams its own contiguous range of chunks,
+// kU chunks in flight per thread.  Under delayed scaling amax_in is an earlier tensor's maximum and values beyond Q * scale
 // saturate; kTrack merges this tensor's maximum into amax_out in the same pass (an atomic maximum
 // per block, skipped when amax_out already holds as much).  Division: the fast exact form when the
 // scale is in [2^-60, 2^60], else the full one.  Elements are first clamped to +-2 Q scale, which
@@ -861,26 +861,26 @@ __global__ __launch_bounds__(256) void quant_tensor_kernel(const void* __restric
     const bool fast = in_pow2_range<-60, 60>(sc);
     const float rsc = fast ? div_rn(1.0f, sc) : 0.0f;
     const float lim = 2.0f * qmax<kFp8>() * sc;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    const int64_t lo = block_range_lo(nchunk), hi = block_range_hi(nchunk);
     float m = 0.0f;
-    for (int64_t c0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c0 < nchunk; c0 += kU * stride) {
+    for (int64_t c0 = lo + threadIdx.x; c0 < hi; c0 += kU * blockDim.x) {
         Raw8<kBf16> raw[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const int64_t c = c0 + u * stride;
-            raw[u] = load_raw8<kBf16>(a, (c < nchunk ? c : nchunk - 1) * 8);
+            const int64_t c = c0 + u * blockDim.x;
+            raw[u] = load_raw8<kBf16>(a, (c < hi ? c : hi - 1) * 8);
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const int64_t c = c0 + u * stride;
+            const int64_t c = c0 + u * blockDim.x;
             float v[8];
             unpack8<kBf16>(raw[u], v);
             if constexpr (kTrack) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
             }
-            if (c >= nchunk) continue;
-            uint32_t lo = 0, hi = 0;
+            if (c >= hi) continue;
+            uint32_t clo = 0, chi = 0;
             if (sc != 0.0f) {                   // a zero scale gives zero codes
                 float qv[8];
 #pragma unroll
@@ -888,10 +888,10 @@ __global__ __launch_bounds__(256) void quant_tensor_kernel(const void* __restric
                     const float t = fminf(fmaxf(v[e], -lim), lim);
                     qv[e] = fast ? div_by_rcp<kFp8>(t, sc, rsc) : div_rn(t, sc);
                 }
-                lo = pack_codes4<kFp8>(qv[0], qv[1], qv[2], qv[3]);
-                hi = pack_codes4<kFp8>(qv[4], qv[5], qv[6], qv[7]);
+                clo = pack_codes4<kFp8>(qv[0], qv[1], qv[2], qv[3]);
+                chi = pack_codes4<kFp8>(qv[4], qv[5], qv[6], qv[7]);
             }
-            *reinterpret_cast<uint2*>(q + c * 8) = make_uint2(lo, hi);
+            *reinterpret_cast<uint2*>(q + c * 8) = make_uint2(clo, chi);
         }
     }
     if constexpr (kTrack) {
