@@ -179,6 +179,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // One 16-byte-per-lane copy into LDS bytes [lds, lds + 1024): lane l writes lds + 16 l.
+//
+// Written as inline asm rather than the compiler's LDS-DMA builtin: the compiler cannot tell which
+// stage a DMA writes, so before any LDS read that follows one it waits for every copy in flight,
+// which would empty the pipeline each half step.  Here the waits are explicit (wait_copies).  The
+// asm sets M0 (the LDS destination of the DMA); the compiler reserves M0 and warns about the
+// clobber, and these kernels use M0 for nothing else (their gfx950 assembly holds no other write or
+// read of it), so the warning is silenced for these two functions.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void copy_sv(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
@@ -195,6 +204,7 @@ __device__ __forceinline__ void copy_v(uintptr_t src, uint32_t lds) {
         : "s"(lds), "v"(src)
         : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Copies of one K step of a tile: kRows rows x 128 bytes.  One wave instruction fills 1 KB of LDS
 // (8 rows): lane l lands at row l / 8 of the block, stored chunk l % 8, which holds the logical
