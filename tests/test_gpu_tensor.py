@@ -78,6 +78,26 @@ def test_quant_act_tensor_current(f, qtype, M, K, dtype):
 
 
 @pytest.mark.parametrize("qtype", ["int8", "fp8"])
+def test_tensor_path_full_grids(f, qtype):
+    """A tensor of 4099 x 8192 bf16 (33.6 M elements): the maximum and the codes run on their full
+    grids (1024 and 4096 blocks), each block streaming its own contiguous range of chunks over
+    several loop passes, with a shorter last range.  Maximum, scale, codes and the maximum tracked
+    in the same pass bit-exact."""
+    announce(f"tensor path full grids {qtype}")
+    X = inputs(4099, 8192, "bf16", seed=23, outliers=20)
+    x = dev(X)
+    amax = f.w8a8_absmax(x)
+    xq, sc, amax_out = f.w8a8_quant_act_tensor(x, amax, qtype, track=True)
+    torch.cuda.synchronize()
+    a_ref = oracle.absmax_tensor(X)
+    assert host(amax)[0] == a_ref
+    assert host(amax_out)[0] == a_ref
+    q_ref, sc_ref = oracle.quant_tensor(X, a_ref, qtype)
+    assert host(sc)[0] == sc_ref
+    np.testing.assert_array_equal(codes(host(xq)), codes(q_ref))
+
+
+@pytest.mark.parametrize("qtype", ["int8", "fp8"])
 @pytest.mark.parametrize("factor", [0.25, 3.0])
 def test_quant_act_tensor_delayed(f, qtype, factor):
     """Delayed scaling: the scale from an earlier maximum (smaller: values saturate; larger: none
