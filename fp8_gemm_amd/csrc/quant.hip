@@ -11,15 +11,16 @@ namespace w8a8 {
 
 namespace {
 
-// ---- activations: one wave per row ---------------------------------------------------------------
+// ---- activations: a row held in the registers of one, two or four waves --------------------------
 //
-// A block of kActWaves waves quantizes whole rows, each wave `rows_per_wave` of them in turn.  The
-// block first stages s and its correctly rounded reciprocals in LDS, so that every X / s and every
-// X~ / scale is a five-operation correctly rounded division (div_by_rcp) instead of a full one.
-// A row is read once from HBM into registers (kChunks 16-byte chunks of 8 elements per lane), lane
-// l owning chunks l, l + 64, ..., so that each load instruction of the wave reads 512 consecutive
-// elements; it is divided by s, reduced to its maximum with a wave butterfly, and quantized from
-// registers.
+// A block of kActWaves waves quantizes whole rows: kSplit consecutive waves share a row, and each
+// group takes `rows_per_wave` rows in turn.  The block first stages s and its correctly rounded
+// reciprocals in LDS, so that every X / s and every X~ / scale is a five-operation correctly
+// rounded division (div_by_rcp) instead of a full one.  A row is read once from HBM into registers
+// (kChunks 16-byte chunks of 8 elements per lane), the lanes of the kSplit waves owning
+// interleaved chunks, so that each load instruction of a wave reads 512 consecutive elements; it is
+// divided by s, reduced to its maximum with a wave butterfly and, across the row's waves, through
+// LDS, and quantized from registers.
 //
 // Fast-division guards (outside them the full division is used, with identical results):
 //   - every s[j] of the block in [2^-20, 2^20];
