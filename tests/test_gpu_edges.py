@@ -285,29 +285,50 @@ def test_alpha(f, alpha):
     check_layer(run_layer(f, X, W, alpha=alpha), X, W, alpha=alpha)
 
 
-def test_e4m3_conversion_sweep(f):
-    """fp32 -> E4M3 on the GPU against the oracle over a dense sweep of fp32 bit patterns in
-    [-448, 448] (every 61st pattern, all signs), plus every E4M3 midpoint.  Each row starts with 448,
-    so its scale is exactly 1 and the code is that of the value itself."""
-    announce("e4m3 sweep")
-    top = np.uint32(0x43E00000)  # 448.0
-    pats = np.arange(0, int(top) + 1, 61, dtype=np.uint32)
+def e4m3_sweep_values():
+    """fp32 values for the E4M3 conversion sweep, all in [-448, 448]:
+    - every 61st fp32 bit pattern from 0 to 448;
+    - every fp32 pattern of the binades where the rounding is decided differently: below the
+      smallest subnormal (2^-12 .. 2^-9, ties to zero at 2^-10), the subnormals (2^-9 .. 2^-6),
+      the first normal binade, [1, 2), and the top binade [256, 448];
+    - every representable E4M3 value, every midpoint between two neighbours, and the fp32
+      patterns one and two ulps on either side of both;
+    each with both signs."""
+    top = np.uint32(0x43E00000)                       # 448.0
+    parts = [np.arange(0, int(top) + 1, 61, dtype=np.uint32)]
+    for lo, hi in ((2.0 ** -12, 2.0 ** -5), (1.0, 2.0), (256.0, 448.0)):
+        a = np.float32(lo).view(np.uint32)
+        b = np.float32(hi).view(np.uint32)
+        parts.append(np.arange(int(a), int(b) + 1, dtype=np.uint32))
+    dec = np.array([oracle.e4m3_decode(c) for c in range(127)], np.float64)   # codes 0 .. 0x7E, ascending
+    mids = (dec[:-1] + dec[1:]) / 2
+    centres = np.concatenate([dec, mids]).astype(np.float32).view(np.uint32).astype(np.int64)
+    for d in (-2, -1, 0, 1, 2):
+        c = centres + d
+        parts.append(c[(c >= 0) & (c <= int(top))].astype(np.uint32))
+    pats = np.unique(np.concatenate(parts))
     vals = pats.view(np.float32)
-    mids = []
-    dec = [oracle.e4m3_decode(c) for c in range(127)]
-    for a, b in zip(dec[:-1], dec[1:]):
-        mids.append((a + b) / 2)
-    vals = np.concatenate([vals, -vals, np.float32(mids), -np.float32(mids)]).astype(np.float32)
+    return np.concatenate([vals, -vals]).astype(np.float32)
+
+
+def test_e4m3_conversion_sweep(f):
+    """fp32 -> E4M3 on the GPU against the oracle over e4m3_sweep_values().  Each row starts with
+    448, so its scale is exactly 1 and the code is that of the value itself."""
+    announce("e4m3 sweep")
+    vals = e4m3_sweep_values()
     K = 4096
     n = (len(vals) + K - 2) // (K - 1)
     pad = np.zeros(n * (K - 1) - len(vals), np.float32)
     body = np.concatenate([vals, pad]).reshape(n, K - 1)
     X = np.concatenate([np.full((n, 1), 448.0, np.float32), body], axis=1)
-    xq, sx = f.w8a8_quant_act(dev(X), None, "fp8")
-    xq, sx = host(xq), host(sx)
-    assert np.all(sx == 1.0)
-    ref, _ = oracle.quant_act(X, None, "fp8")
-    np.testing.assert_array_equal(xq, ref)
+    announce(f"e4m3 sweep: {len(vals)} values in {n} rows")
+    for r0 in range(0, n, 8192):               # bounded device and host memory per launch
+        Xb = X[r0:r0 + 8192]
+        xq, sx = f.w8a8_quant_act(dev(Xb), None, "fp8")
+        xq, sx = host(xq), host(sx)
+        assert np.all(sx == 1.0)
+        ref, _ = oracle.quant_act(Xb, None, "fp8")
+        np.testing.assert_array_equal(xq, ref)
 
 
 def test_int8_extremes_and_determinism(f):
