@@ -18,17 +18,11 @@ import os
 
 import torch
 
+from . import _cabi
 from .build import LIB_PATH
 
-W8A8_OK, W8A8_ERR_INVALID_ARG, W8A8_ERR_UNSUPPORTED, W8A8_ERR_HIP = 0, 1, 2, 3
-W8A8_F32, W8A8_BF16 = 0, 1
-W8A8_INT8, W8A8_FP8_E4M3 = 0, 1
-
-ENTRY_POINTS = ("w8a8_smooth_scales", "w8a8_fold_quant_weight", "w8a8_quant_act", "w8a8_smooth_quant",
-                "w8a8_gemm_dequant",
-                "w8a8_gemm_i32", "w8a8_gemm_f32", "w8a8_absmax", "w8a8_quant_act_tensor",
-                "w8a8_quant_weight_tensor", "w8a8_gemm_dequant_tensor", "w8a8_gemm_w8a16", "w8a8_fold_norm_gain",
-                "w8a8_norm_quant_act", "w8a8_layer_norm_quant_act", "w8a8_status_string", "w8a8_version")
+from ._cabi import (ENTRY_POINTS, W8A8_BF16, W8A8_ERR_HIP, W8A8_ERR_INVALID_ARG,  # noqa: F401
+                    W8A8_ERR_UNSUPPORTED, W8A8_F32, W8A8_FP8_E4M3, W8A8_INT8, W8A8_OK)
 
 
 class W8A8Error(RuntimeError):
@@ -46,32 +40,8 @@ def _load() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libw8a8 is not built ({LIB_PATH} missing); run `python -m fp8_gemm_amd.build`")
-    lib = ctypes.CDLL(LIB_PATH)
-    P, I64, I, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
-    sigs = {
-        "w8a8_smooth_scales": (I, [P, I, I64, I64, P, I, I64, F, P, P, I, P, P]),
-        "w8a8_fold_quant_weight": (I, [P, I, I64, I64, P, I, P, P, P]),
-        "w8a8_quant_act": (I, [P, I, I64, I64, P, I, P, P, P]),
-        "w8a8_smooth_quant": (I, [P, I, I64, I64, P, I, I64, F, I, P, P, P, P, P, P, P, P]),
-        "w8a8_gemm_dequant": (I, [P, P, P, P, I, I64, I64, I64, P, P]),
-        "w8a8_gemm_i32": (I, [P, P, I64, I64, I64, P, P]),
-        "w8a8_gemm_f32": (I, [P, P, I64, I64, I64, P, P]),
-        "w8a8_absmax": (I, [P, I, I64, P, I, P]),
-        "w8a8_quant_act_tensor": (I, [P, I, I64, I64, P, I, P, P, P, I, P]),
-        "w8a8_quant_weight_tensor": (I, [P, I, I64, I64, I, P, P, P]),
-        "w8a8_gemm_dequant_tensor": (I, [P, P, P, P, I, I64, I64, I64, P, P]),
-        "w8a8_gemm_w8a16": (I, [P, P, P, I64, I64, I64, P, P]),
-        "w8a8_fold_norm_gain": (I, [P, P, I64, P, P]),
-        "w8a8_norm_quant_act": (I, [P, I, I64, I64, P, F, I, P, P, P]),
-        "w8a8_layer_norm_quant_act": (I, [P, I, I64, I64, P, P, F, I, P, P, P]),
-        "w8a8_status_string": (ctypes.c_char_p, [I]),
-        "w8a8_version": (ctypes.c_char_p, []),
-    }
-    for name, (res, args) in sigs.items():
-        fn = getattr(lib, name)
-        fn.restype, fn.argtypes = res, args
-    _lib = lib
-    return lib
+    _lib = _cabi.load(LIB_PATH)
+    return _lib
 
 
 def lib_path() -> str:
@@ -117,10 +87,37 @@ def _code_dtype(q: int):
     return torch.int8 if q == W8A8_INT8 else torch.uint8
 
 
-def _dev(t, what):
-    if t is not None and (not t.is_cuda or not t.is_contiguous()):
+_CODES = (torch.int8, torch.uint8, torch.float8_e4m3fn)   # one byte per code
+_F32 = (torch.float32,)
+
+
+def _arg(t, what, dtypes=None, shape=None):
+    """A tensor argument: None, or a contiguous GPU tensor of one of dtypes whose shape is shape
+    (an int checks the element count).  Checked before any pointer reaches the library, so that a
+    wrong size or element type is a Python error and not an out-of-bounds device access."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{what} must be a contiguous GPU tensor")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{what} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if isinstance(shape, int):
+        if t.numel() != shape:
+            raise ValueError(f"{what} must have {shape} elements, got {t.numel()}")
+    elif shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     return t
+
+
+def _mat(t, what, dtypes):
+    """A 2-D tensor argument; returns (tensor, rows, cols)."""
+    _arg(t, what, dtypes)
+    if t.dim() != 2:
+        raise ValueError(f"{what} must be 2-D, got shape {tuple(t.shape)}")
+    return t, t.shape[0], t.shape[1]
+
+
+_FLOAT_IN = (torch.float32, torch.bfloat16)
 
 
 def _check(fn: str, status: int):
@@ -128,20 +125,25 @@ def _check(fn: str, status: int):
         raise W8A8Error(fn, status)
 
 
+def _out(t, what, dtypes, shape, device):
+    """An output: allocated when None, else checked like an argument."""
+    if t is None:
+        return torch.empty(shape, dtype=dtypes[0], device=device)
+    return _arg(t, what, dtypes, shape)
+
+
 # ---- entry points ------------------------------------------------------------------------------
 
 def w8a8_smooth_scales(x, w, alpha: float = 0.5, ax=None, aw=None, s=None, accumulate: bool = False,
                        stream=None):
     """Calibration maxima and SmoothQuant factors; returns (ax, aw, s), each float32 [K]."""
-    _dev(x, "x"), _dev(w, "w")
-    M, K = x.shape
-    K2, N = w.shape
+    _, M, K = _mat(x, "x", _FLOAT_IN)
+    _, K2, N = _mat(w, "w", _FLOAT_IN)
     if K2 != K:
         raise ValueError("x is [M, K] and w is [K, N]")
-    dev = x.device
-    ax = torch.empty(K, dtype=torch.float32, device=dev) if ax is None else _dev(ax, "ax")
-    aw = torch.empty(K, dtype=torch.float32, device=dev) if aw is None else _dev(aw, "aw")
-    s = torch.empty(K, dtype=torch.float32, device=dev) if s is None else _dev(s, "s")
+    ax = _out(ax, "ax", _F32, K, x.device)
+    aw = _out(aw, "aw", _F32, K, x.device)
+    s = _out(s, "s", _F32, K, x.device)
     _check("w8a8_smooth_scales", _load().w8a8_smooth_scales(
         _ptr(x), _dtype(x), M, K, _ptr(w), _dtype(w), N, float(alpha), _ptr(ax), _ptr(aw),
         int(bool(accumulate)), _ptr(s), _stream(stream)))
@@ -150,11 +152,11 @@ def w8a8_smooth_scales(x, w, alpha: float = 0.5, ax=None, aw=None, s=None, accum
 
 def w8a8_fold_quant_weight(w, s=None, qtype="int8", wq=None, w_scale=None, stream=None):
     """W [K, N] -> (codes [N, K], per-output-channel scales float32 [N])."""
-    _dev(w, "w"), _dev(s, "s")
+    _, K, N = _mat(w, "w", _FLOAT_IN)
+    _arg(s, "s", _F32, K)
     q = _qtype(qtype)
-    K, N = w.shape
-    wq = torch.empty((N, K), dtype=_code_dtype(q), device=w.device) if wq is None else _dev(wq, "wq")
-    w_scale = torch.empty(N, dtype=torch.float32, device=w.device) if w_scale is None else _dev(w_scale, "w_scale")
+    wq = _out(wq, "wq", (_code_dtype(q),) + _CODES, (N, K), w.device)
+    w_scale = _out(w_scale, "w_scale", _F32, N, w.device)
     _check("w8a8_fold_quant_weight", _load().w8a8_fold_quant_weight(
         _ptr(w), _dtype(w), K, N, _ptr(s), q, _ptr(wq), _ptr(w_scale), _stream(stream)))
     return wq, w_scale
@@ -162,11 +164,11 @@ def w8a8_fold_quant_weight(w, s=None, qtype="int8", wq=None, w_scale=None, strea
 
 def w8a8_quant_act(x, s=None, qtype="int8", xq=None, x_scale=None, stream=None):
     """X [M, K] -> (codes [M, K], per-token scales float32 [M])."""
-    _dev(x, "x"), _dev(s, "s")
+    _, M, K = _mat(x, "x", _FLOAT_IN)
+    _arg(s, "s", _F32, K)
     q = _qtype(qtype)
-    M, K = x.shape
-    xq = torch.empty((M, K), dtype=_code_dtype(q), device=x.device) if xq is None else _dev(xq, "xq")
-    x_scale = torch.empty(M, dtype=torch.float32, device=x.device) if x_scale is None else _dev(x_scale, "x_scale")
+    xq = _out(xq, "xq", (_code_dtype(q),) + _CODES, (M, K), x.device)
+    x_scale = _out(x_scale, "x_scale", _F32, M, x.device)
     _check("w8a8_quant_act", _load().w8a8_quant_act(
         _ptr(x), _dtype(x), M, K, _ptr(s), q, _ptr(xq), _ptr(x_scale), _stream(stream)))
     return xq, x_scale
@@ -176,20 +178,17 @@ def w8a8_smooth_quant(x, w, alpha: float = 0.5, qtype="int8", out=None, stream=N
     """Calibration, smoothing factors, weight fold + quantize and activation quantize in one call.
     Returns a dict ax, aw, s [K], wq [N, K], w_scale [N], xq [M, K], x_scale [M] (``out``: a dict
     of such tensors to write into)."""
-    _dev(x, "x"), _dev(w, "w")
-    q = _qtype(qtype)
-    M, K = x.shape
-    K2, N = w.shape
+    _, M, K = _mat(x, "x", _FLOAT_IN)
+    _, K2, N = _mat(w, "w", _FLOAT_IN)
     if K2 != K:
         raise ValueError("x is [M, K] and w is [K, N]")
-    dev = x.device
-    if out is None:
-        f32 = dict(dtype=torch.float32, device=dev)
-        out = dict(ax=torch.empty(K, **f32), aw=torch.empty(K, **f32), s=torch.empty(K, **f32),
-                   wq=torch.empty((N, K), dtype=_code_dtype(q), device=dev), w_scale=torch.empty(N, **f32),
-                   xq=torch.empty((M, K), dtype=_code_dtype(q), device=dev), x_scale=torch.empty(M, **f32))
-    for name in ("ax", "aw", "s", "wq", "w_scale", "xq", "x_scale"):
-        _dev(out[name], name)
+    q = _qtype(qtype)
+    codes = (_code_dtype(q),) + _CODES
+    want = dict(ax=(_F32, K), aw=(_F32, K), s=(_F32, K), wq=(codes, (N, K)), w_scale=(_F32, N),
+                xq=(codes, (M, K)), x_scale=(_F32, M))
+    out = {} if out is None else dict(out)
+    for name, (dts, shape) in want.items():
+        out[name] = _out(out.get(name), name, dts, shape, x.device)
     _check("w8a8_smooth_quant", _load().w8a8_smooth_quant(
         _ptr(x), _dtype(x), M, K, _ptr(w), _dtype(w), N, float(alpha), q, _ptr(out["ax"]), _ptr(out["aw"]),
         _ptr(out["s"]), _ptr(out["wq"]), _ptr(out["w_scale"]), _ptr(out["xq"]), _ptr(out["x_scale"]),
@@ -197,16 +196,21 @@ def w8a8_smooth_quant(x, w, alpha: float = 0.5, qtype="int8", out=None, stream=N
     return out
 
 
-def w8a8_gemm_dequant(xq, x_scale, wq, w_scale, qtype="int8", y=None, stream=None):
-    """Quantized GEMM + dequantize: returns Y bfloat16 [M, N]."""
-    for t, n in ((xq, "xq"), (x_scale, "x_scale"), (wq, "wq"), (w_scale, "w_scale")):
-        _dev(t, n)
-    q = _qtype(qtype)
-    M, K = xq.shape
-    N, K2 = wq.shape
+def _gemm_operands(xq, wq):
+    _, M, K = _mat(xq, "xq", _CODES)
+    _, N, K2 = _mat(wq, "wq", _CODES)
     if K2 != K:
         raise ValueError("xq is [M, K] and wq is [N, K]")
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device) if y is None else _dev(y, "y")
+    return M, N, K
+
+
+def w8a8_gemm_dequant(xq, x_scale, wq, w_scale, qtype="int8", y=None, stream=None):
+    """Quantized GEMM + dequantize: returns Y bfloat16 [M, N]."""
+    M, N, K = _gemm_operands(xq, wq)
+    _arg(x_scale, "x_scale", _F32, M)
+    _arg(w_scale, "w_scale", _F32, N)
+    q = _qtype(qtype)
+    y = _out(y, "y", (torch.bfloat16,), (M, N), xq.device)
     _check("w8a8_gemm_dequant", _load().w8a8_gemm_dequant(
         _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), q, M, N, K, _ptr(y), _stream(stream)))
     return y
@@ -214,24 +218,16 @@ def w8a8_gemm_dequant(xq, x_scale, wq, w_scale, qtype="int8", y=None, stream=Non
 
 def w8a8_gemm_i32(xq, wq, acc=None, stream=None):
     """INT8 GEMM without the epilogue: int32 [M, N] accumulators."""
-    _dev(xq, "xq"), _dev(wq, "wq")
-    M, K = xq.shape
-    N, K2 = wq.shape
-    if K2 != K:
-        raise ValueError("xq is [M, K] and wq is [N, K]")
-    acc = torch.empty((M, N), dtype=torch.int32, device=xq.device) if acc is None else _dev(acc, "acc")
+    M, N, K = _gemm_operands(xq, wq)
+    acc = _out(acc, "acc", (torch.int32,), (M, N), xq.device)
     _check("w8a8_gemm_i32", _load().w8a8_gemm_i32(_ptr(xq), _ptr(wq), M, N, K, _ptr(acc), _stream(stream)))
     return acc
 
 
 def w8a8_gemm_f32(xq, wq, acc=None, stream=None):
     """E4M3 GEMM without the epilogue: the matrix cores' fp32 [M, N] accumulators."""
-    _dev(xq, "xq"), _dev(wq, "wq")
-    M, K = xq.shape
-    N, K2 = wq.shape
-    if K2 != K:
-        raise ValueError("xq is [M, K] and wq is [N, K]")
-    acc = torch.empty((M, N), dtype=torch.float32, device=xq.device) if acc is None else _dev(acc, "acc")
+    M, N, K = _gemm_operands(xq, wq)
+    acc = _out(acc, "acc", _F32, (M, N), xq.device)
     _check("w8a8_gemm_f32", _load().w8a8_gemm_f32(_ptr(xq), _ptr(wq), M, N, K, _ptr(acc), _stream(stream)))
     return acc
 
@@ -255,8 +251,8 @@ def w8a8_layer(x, w, alpha: float = 0.5, qtype="int8", fused: bool = True, strea
 
 def w8a8_absmax(a, amax=None, accumulate: bool = False, stream=None):
     """max |a| over the whole tensor, into a float32 [1] tensor (merged with it if accumulate)."""
-    _dev(a, "a")
-    amax = torch.empty(1, dtype=torch.float32, device=a.device) if amax is None else _dev(amax, "amax")
+    _arg(a, "a", _FLOAT_IN)
+    amax = _out(amax, "amax", _F32, 1, a.device)
     _check("w8a8_absmax", _load().w8a8_absmax(_ptr(a), _dtype(a), a.numel(), _ptr(amax), int(bool(accumulate)),
                                               _stream(stream)))
     return amax
@@ -266,14 +262,13 @@ def w8a8_quant_act_tensor(x, amax_in, qtype="fp8", xq=None, x_scale=None, amax_o
                           accumulate: bool = False, stream=None):
     """X [M, K] -> (codes [M, K], the one scale float32 [1], amax_out or None) with the scale
     amax_in / Q.  track: also return this X's maximum (for the next step's amax_in)."""
-    _dev(x, "x"), _dev(amax_in, "amax_in")
+    _, M, K = _mat(x, "x", _FLOAT_IN)
+    _arg(amax_in, "amax_in", _F32, 1)
     q = _qtype(qtype)
-    M, K = x.shape
-    xq = torch.empty((M, K), dtype=_code_dtype(q), device=x.device) if xq is None else _dev(xq, "xq")
-    x_scale = torch.empty(1, dtype=torch.float32, device=x.device) if x_scale is None else _dev(x_scale, "x_scale")
-    if track and amax_out is None:
-        amax_out = torch.empty(1, dtype=torch.float32, device=x.device)
-    _dev(amax_out, "amax_out")
+    xq = _out(xq, "xq", (_code_dtype(q),) + _CODES, (M, K), x.device)
+    x_scale = _out(x_scale, "x_scale", _F32, 1, x.device)
+    if track or amax_out is not None:
+        amax_out = _out(amax_out, "amax_out", _F32, 1, x.device)
     _check("w8a8_quant_act_tensor", _load().w8a8_quant_act_tensor(
         _ptr(x), _dtype(x), M, K, _ptr(amax_in), q, _ptr(xq), _ptr(x_scale), _ptr(amax_out),
         int(bool(accumulate)), _stream(stream)))
@@ -282,11 +277,10 @@ def w8a8_quant_act_tensor(x, amax_in, qtype="fp8", xq=None, x_scale=None, amax_o
 
 def w8a8_quant_weight_tensor(w, qtype="fp8", wq=None, w_scale=None, stream=None):
     """W [K, N] -> (codes [N, K], the one scale float32 [1] = max|W| / Q)."""
-    _dev(w, "w")
+    _, K, N = _mat(w, "w", _FLOAT_IN)
     q = _qtype(qtype)
-    K, N = w.shape
-    wq = torch.empty((N, K), dtype=_code_dtype(q), device=w.device) if wq is None else _dev(wq, "wq")
-    w_scale = torch.empty(1, dtype=torch.float32, device=w.device) if w_scale is None else _dev(w_scale, "w_scale")
+    wq = _out(wq, "wq", (_code_dtype(q),) + _CODES, (N, K), w.device)
+    w_scale = _out(w_scale, "w_scale", _F32, 1, w.device)
     _check("w8a8_quant_weight_tensor", _load().w8a8_quant_weight_tensor(
         _ptr(w), _dtype(w), K, N, q, _ptr(wq), _ptr(w_scale), _stream(stream)))
     return wq, w_scale
@@ -294,14 +288,11 @@ def w8a8_quant_weight_tensor(w, qtype="fp8", wq=None, w_scale=None, stream=None)
 
 def w8a8_gemm_dequant_tensor(xq, x_scale, wq, w_scale, qtype="fp8", y=None, stream=None):
     """Quantized GEMM + dequantize with one scale per operand: Y bfloat16 [M, N]."""
-    for t, n in ((xq, "xq"), (x_scale, "x_scale"), (wq, "wq"), (w_scale, "w_scale")):
-        _dev(t, n)
+    M, N, K = _gemm_operands(xq, wq)
+    _arg(x_scale, "x_scale", _F32, 1)
+    _arg(w_scale, "w_scale", _F32, 1)
     q = _qtype(qtype)
-    M, K = xq.shape
-    N, K2 = wq.shape
-    if K2 != K:
-        raise ValueError("xq is [M, K] and wq is [N, K]")
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device) if y is None else _dev(y, "y")
+    y = _out(y, "y", (torch.bfloat16,), (M, N), xq.device)
     _check("w8a8_gemm_dequant_tensor", _load().w8a8_gemm_dequant_tensor(
         _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), q, M, N, K, _ptr(y), _stream(stream)))
     return y
@@ -326,15 +317,12 @@ def w8a8_layer_tensor(x, w, qtype="fp8", amax_prev=None, stream=None):
 def w8a8_gemm_w8a16(x, wq, w_scale, y=None, stream=None):
     """bf16 X [M, K] times INT8 weights (wq [N, K], per-channel w_scale [N]) on the bf16 matrix
     cores: Y bfloat16 [M, N] = w_scale[n] * sum_k x[m, k] wq[n, k]."""
-    for t, n in ((x, "x"), (wq, "wq"), (w_scale, "w_scale")):
-        _dev(t, n)
-    if x.dtype != torch.bfloat16 or wq.dtype != torch.int8:
-        raise TypeError("w8a8_gemm_w8a16 takes bf16 x and int8 wq")
-    M, K = x.shape
-    N, K2 = wq.shape
+    _, M, K = _mat(x, "x", (torch.bfloat16,))
+    _, N, K2 = _mat(wq, "wq", (torch.int8,))
     if K2 != K:
         raise ValueError("x is [M, K] and wq is [N, K]")
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else _dev(y, "y")
+    _arg(w_scale, "w_scale", _F32, N)
+    y = _out(y, "y", (torch.bfloat16,), (M, N), x.device)
     _check("w8a8_gemm_w8a16", _load().w8a8_gemm_w8a16(_ptr(x), _ptr(wq), _ptr(w_scale), M, N, K, _ptr(y),
                                                       _stream(stream)))
     return y
@@ -344,10 +332,13 @@ def w8a8_gemm_w8a16(x, wq, w_scale, y=None, stream=None):
 
 def w8a8_fold_norm_gain(g, s, out=None, stream=None):
     """g' = g / s (either may be None = 1): float32 [K]."""
-    _dev(g, "g"), _dev(s, "s")
     ref = g if g is not None else s
-    K = ref.numel()
-    out = torch.empty(K, dtype=torch.float32, device=ref.device) if out is None else _dev(out, "out")
+    if ref is None:
+        raise ValueError("w8a8_fold_norm_gain needs g or s")
+    K = _arg(ref, "g" if g is not None else "s", _F32).numel()
+    _arg(g, "g", _F32, K)
+    _arg(s, "s", _F32, K)
+    out = _out(out, "out", _F32, K, ref.device)
     _check("w8a8_fold_norm_gain", _load().w8a8_fold_norm_gain(_ptr(g), _ptr(s), K, _ptr(out), _stream(stream)))
     return out
 
@@ -355,11 +346,11 @@ def w8a8_fold_norm_gain(g, s, out=None, stream=None):
 def w8a8_norm_quant_act(h, g=None, eps: float = 1e-5, qtype="int8", xq=None, x_scale=None, stream=None):
     """RMS norm of h [M, K] with gain g (1/s folded in), then per-token quantize:
     (codes [M, K], scales float32 [M])."""
-    _dev(h, "h"), _dev(g, "g")
+    _, M, K = _mat(h, "h", _FLOAT_IN)
+    _arg(g, "g", _F32, K)
     q = _qtype(qtype)
-    M, K = h.shape
-    xq = torch.empty((M, K), dtype=_code_dtype(q), device=h.device) if xq is None else _dev(xq, "xq")
-    x_scale = torch.empty(M, dtype=torch.float32, device=h.device) if x_scale is None else _dev(x_scale, "x_scale")
+    xq = _out(xq, "xq", (_code_dtype(q),) + _CODES, (M, K), h.device)
+    x_scale = _out(x_scale, "x_scale", _F32, M, h.device)
     _check("w8a8_norm_quant_act", _load().w8a8_norm_quant_act(
         _ptr(h), _dtype(h), M, K, _ptr(g), float(eps), q, _ptr(xq), _ptr(x_scale), _stream(stream)))
     return xq, x_scale
@@ -369,11 +360,12 @@ def w8a8_layer_norm_quant_act(h, g=None, b=None, eps: float = 1e-5, qtype="int8"
                               stream=None):
     """LayerNorm of h [M, K] with gain g and bias b (1/s folded into both), then per-token
     quantize: (codes [M, K], scales float32 [M])."""
-    _dev(h, "h"), _dev(g, "g"), _dev(b, "b")
+    _, M, K = _mat(h, "h", _FLOAT_IN)
+    _arg(g, "g", _F32, K)
+    _arg(b, "b", _F32, K)
     q = _qtype(qtype)
-    M, K = h.shape
-    xq = torch.empty((M, K), dtype=_code_dtype(q), device=h.device) if xq is None else _dev(xq, "xq")
-    x_scale = torch.empty(M, dtype=torch.float32, device=h.device) if x_scale is None else _dev(x_scale, "x_scale")
+    xq = _out(xq, "xq", (_code_dtype(q),) + _CODES, (M, K), h.device)
+    x_scale = _out(x_scale, "x_scale", _F32, M, h.device)
     _check("w8a8_layer_norm_quant_act", _load().w8a8_layer_norm_quant_act(
         _ptr(h), _dtype(h), M, K, _ptr(g), _ptr(b), float(eps), q, _ptr(xq), _ptr(x_scale), _stream(stream)))
     return xq, x_scale

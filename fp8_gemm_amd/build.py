@@ -38,9 +38,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libw8a8)")
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+# Address and undefined-behaviour sanitizers on the host code only (the device code is unchanged),
+# for a test build: build(path, obj_dir, HOST_SANITIZE).
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src: str, verbose: bool, obj_dir: str, extra) -> str:
+    obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,19 +59,23 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    os.makedirs(LIB_DIR, exist_ok=True)
+def build(verbose: bool = False, path: str | None = None, obj_dir: str | None = None, extra=()) -> str:
+    """Compile every csrc/*.hip and link the library at path (default LIB_PATH); extra flags go
+    to every compile."""
+    out = LIB_PATH if path is None else path
+    objs_dir = OBJ_DIR if obj_dir is None else obj_dir
+    os.makedirs(objs_dir, exist_ok=True)
+    os.makedirs(os.path.dirname(out), exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
+        objs = list(ex.map(lambda s: _compile(s, verbose, objs_dir, extra), srcs))
+    tmp = out + f".tmp{os.getpid()}"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -105,9 +105,10 @@ __device__ __forceinline__ float div_rn(float a, float b) { return __fdiv_rn(a, 
 // remainders are exact when nothing underflows: callers use this only where |b| and the quotients
 // that can affect a result lie well inside the normal range, and fall back to div_rn elsewhere.
 // The corrections turn a zero quotient into +0; kZeroSign restores the sign of a zero quotient
-// from q0 (needed where the sign of zero reaches a result, as in E4M3 codes).
+// from q0 (needed where the sign of zero reaches a result, as in E4M3 codes).  Host-callable so
+// that the same arithmetic can be checked against IEEE division on the CPU.
 template <bool kZeroSign = true>
-__device__ __forceinline__ float div_by_rcp(float a, float b, float rb) {
+__host__ __device__ __forceinline__ float div_by_rcp(float a, float b, float rb) {
     const float q0 = a * rb;
     const float r0 = __builtin_fmaf(-q0, b, a);
     const float q1 = __builtin_fmaf(r0, rb, q0);
@@ -118,7 +119,7 @@ __device__ __forceinline__ float div_by_rcp(float a, float b, float rb) {
 
 // Divisors for which div_by_rcp is used: 2^lo <= |b| <= 2^hi.
 template <int kLo, int kHi>
-__device__ __forceinline__ bool in_pow2_range(float b) {
+__host__ __device__ __forceinline__ bool in_pow2_range(float b) {
     const float m = fabsf(b);
     return m >= __builtin_ldexpf(1.0f, kLo) && m <= __builtin_ldexpf(1.0f, kHi);
 }

@@ -1,5 +1,5 @@
 // Quantized GEMM with the dequantizing epilogue on the gfx950 matrix cores.
-// ("Weight-Activation Quantization", section 3 step 2: Y = dequantize(X_int8 @ W_int8); section 4:
+// ("Weight-Activation Quantization", section 3 step 2: the product of the code matrices, dequantized; section 4:
 // x^ = s q for E4M3.)
 //
 // Both operands are K-contiguous: xq [M, K] and wq [N, K].  Matrix-core instructions:

@@ -1,6 +1,6 @@
 // Activation smooth + per-token quantize, and the weight quantize-and-transpose.
 // ("Weight-Activation Quantization", section 3: divide activation channel j by s_j, multiply
-// weight channel j by s_j, then X_int8 = quantize(X_tilde), W_int8 = quantize(W_tilde); section 2:
+// weight channel j by s_j, then both smoothed operands are quantized to 8 bits; section 2:
 // symmetric INT8 with scale = absmax / 127; section 4: E4M3 with scale = absmax / 448.)
 #include <algorithm>
 
@@ -27,7 +27,9 @@ namespace {
 //   - the row scale in [2^-60, 2^60].
 // Then every element whose code can be nonzero, and the row maximum, has X~ >= 2^-10 * scale >=
 // 2^-70 and X >= 2^-90, so all quotients and remainders are normal numbers and exact; elements
-// below that bound give code 0 on either path.
+// below that bound give code 0 on either path.  The row scale is only known after the quotients,
+// so a block in which a row's scale comes out of that range (or zero) after fast divisions is
+// quantized again with full divisions, which rewrites the same codes and scales.
 constexpr int kActWaves = 8;
 
 // LDS layout of s and 1/s: for chunk c (elements 8c .. 8c + 7), the low halves 8c .. 8c + 3 of all
@@ -126,48 +128,65 @@ __device__ __forceinline__ void quant_act_body(const void* __restrict__ x, const
     const int part = wave % kSplit;
     const int lane_c = part * kWave + lane;     // first chunk of this wave's share
     constexpr int kStride = kSplit * kWave;
-    for (int rr = 0; rr < rows_per_wave; ++rr) {
-        const int64_t row = (bx * rows_per_wave + rr) * kRowsPerPass + slot;
-        const bool live = row < M;
-        if (kSplit == 1 && !live) break;
-        const int64_t rrow = live ? row : M - 1;
-        // All loads unconditional (chunks past the row end re-read the last chunk, which changes
-        // no maximum and is never stored) and issued before any conversion, so that they are all
-        // in flight at once.
-        Raw8<kBf16> raw[kChunks];
-#pragma unroll
-        for (int i = 0; i < kChunks; ++i) {
-            int64_t c = lane_c + static_cast<int64_t>(kStride) * i;
-            c = c < nchunk ? c : nchunk - 1;
-            raw[i] = load_raw8<kBf16>(x, rrow * K + c * 8);
-        }
-        float v[kChunks][8];
-#pragma unroll
-        for (int i = 0; i < kChunks; ++i) unpack8<kBf16>(raw[i], v[i]);
-        float amax = fast_s ? smooth_chunks<true, kSmooth, kFp8>(v, sh_s, sh_r, lane_c, kStride, nchunk)
-                            : smooth_chunks<false, kSmooth, kFp8>(v, sh_s, sh_r, lane_c, kStride, nchunk);
-        amax = wave_max(amax);
-        if constexpr (kSplit > 1) {
-            if (lane == 0) xchg[rr & 1][wave] = amax;
-            __syncthreads();
-#pragma unroll
-            for (int p = 0; p < kSplit; ++p) amax = fmaxf(amax, xchg[rr & 1][slot * kSplit + p]);
-        }
-        if (!live) continue;
-        const float sc = div_rn(amax, qmax<kFp8>());
-        if (lane == 0 && part == 0) scale[row] = sc;
-        uint8_t* const qrow = q + row * K;
-        if (sc == 0.0f) {                       // a zero scale gives zero codes
+    // One pass over the block's rows; X / s by div_by_rcp when fast.  Returns whether a row of this
+    // wave came out with a scale outside [2^-60, 2^60] (or zero) after fast divisions: the guard
+    // above does not hold there, so the block then takes a second pass with full divisions, in
+    // which the same lanes rewrite the same codes and scales.
+    auto rows_pass = [&](bool fast) {
+        bool redo = false;
+        for (int rr = 0; rr < rows_per_wave; ++rr) {
+            const int64_t row = (bx * rows_per_wave + rr) * kRowsPerPass + slot;
+            const bool live = row < M;
+            if (kSplit == 1 && !live) break;
+            const int64_t rrow = live ? row : M - 1;
+            // All loads unconditional (chunks past the row end re-read the last chunk, which changes
+            // no maximum and is never stored) and issued before any conversion, so that they are all
+            // in flight at once.
+            Raw8<kBf16> raw[kChunks];
 #pragma unroll
             for (int i = 0; i < kChunks; ++i) {
-                const int64_t c = lane_c + static_cast<int64_t>(kStride) * i;
-                if (c < nchunk) *reinterpret_cast<uint2*>(qrow + c * 8) = make_uint2(0u, 0u);
+                int64_t c = lane_c + static_cast<int64_t>(kStride) * i;
+                c = c < nchunk ? c : nchunk - 1;
+                raw[i] = load_raw8<kBf16>(x, rrow * K + c * 8);
             }
-        } else if (in_pow2_range<-60, 60>(sc)) {
-            store_codes<kFp8, true>(v, sc, div_rn(1.0f, sc), lane_c, kStride, nchunk, qrow);
-        } else {
-            store_codes<kFp8, false>(v, sc, 0.0f, lane_c, kStride, nchunk, qrow);
+            float v[kChunks][8];
+#pragma unroll
+            for (int i = 0; i < kChunks; ++i) unpack8<kBf16>(raw[i], v[i]);
+            float amax = fast ? smooth_chunks<true, kSmooth, kFp8>(v, sh_s, sh_r, lane_c, kStride, nchunk)
+                              : smooth_chunks<false, kSmooth, kFp8>(v, sh_s, sh_r, lane_c, kStride, nchunk);
+            amax = wave_max(amax);
+            if constexpr (kSplit > 1) {
+                if (lane == 0) xchg[rr & 1][wave] = amax;
+                __syncthreads();
+#pragma unroll
+                for (int p = 0; p < kSplit; ++p) amax = fmaxf(amax, xchg[rr & 1][slot * kSplit + p]);
+            }
+            if (!live) continue;
+            const float sc = div_rn(amax, qmax<kFp8>());
+            const bool sc_fast = in_pow2_range<-60, 60>(sc);
+            if (fast && kSmooth && !sc_fast) {
+                redo = true;
+                continue;                       // written by the second pass
+            }
+            if (lane == 0 && part == 0) scale[row] = sc;
+            uint8_t* const qrow = q + row * K;
+            if (sc == 0.0f) {                   // a zero scale gives zero codes
+#pragma unroll
+                for (int i = 0; i < kChunks; ++i) {
+                    const int64_t c = lane_c + static_cast<int64_t>(kStride) * i;
+                    if (c < nchunk) *reinterpret_cast<uint2*>(qrow + c * 8) = make_uint2(0u, 0u);
+                }
+            } else if (sc_fast) {
+                store_codes<kFp8, true>(v, sc, div_rn(1.0f, sc), lane_c, kStride, nchunk, qrow);
+            } else {
+                store_codes<kFp8, false>(v, sc, 0.0f, lane_c, kStride, nchunk, qrow);
+            }
         }
+        return redo;
+    };
+    const bool redo = rows_pass(fast_s);
+    if (kSmooth && fast_s) {                    // fast_s is uniform over the block
+        if (__syncthreads_or(redo)) rows_pass(false);
     }
 }
 

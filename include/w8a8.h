@@ -9,9 +9,9 @@
  *         s2 "The Problem: Activation Outliers"  symmetric INT8, scale = absmax / 127;
  *         s3 "SmoothQuant: The Smoothing Trick"  Y = XW = (X S^-1)(S W), divide activation
  *             channel j by s_j and multiply weight channel j by s_j, smoothing offline then
- *             quantization at inference, Y = dequantize(X_int8 @ W_int8), and
+ *             quantization at inference, the 8-bit product dequantized by the scales, and
  *             s_j = max|X_j|^alpha / max|W_j|^(1-alpha) with alpha in [0, 1];
- *         s4 "FP8 W8A8"  E4M3 operands, range [-448, 448], q = cast_fp8(x / s), x^ = s q,
+ *         s4 "FP8 W8A8"  E4M3 operands, range [-448, 448], codes of x / s, x^ = s q,
  *             s = max|x| / 448.
  *   [ACT] "Define activation quantization ..." (zenaique flashcard): per-token activation and
  *         per-channel weight scaling.
@@ -45,16 +45,25 @@
 extern "C" {
 #endif
 
-typedef enum w8a8_status {
+/* The enumerations are int-sized as in C.  In C++ they get int as their fixed underlying type, so
+ * that any int a caller passes is a value of the type and can be checked (an enumeration without
+ * one cannot hold values outside its enumerators' range); the ABI is the same. */
+#ifdef __cplusplus
+#define W8A8_ENUM_BASE : int
+#else
+#define W8A8_ENUM_BASE
+#endif
+
+typedef enum w8a8_status W8A8_ENUM_BASE {
     W8A8_OK = 0,
     W8A8_ERR_INVALID_ARG = 1,
     W8A8_ERR_UNSUPPORTED = 2,
     W8A8_ERR_HIP = 3
 } w8a8_status;
 
-typedef enum w8a8_dtype { W8A8_F32 = 0, W8A8_BF16 = 1 } w8a8_dtype;
+typedef enum w8a8_dtype W8A8_ENUM_BASE { W8A8_F32 = 0, W8A8_BF16 = 1 } w8a8_dtype;
 
-typedef enum w8a8_qtype { W8A8_INT8 = 0, W8A8_FP8_E4M3 = 1 } w8a8_qtype;
+typedef enum w8a8_qtype W8A8_ENUM_BASE { W8A8_INT8 = 0, W8A8_FP8_E4M3 = 1 } w8a8_qtype;
 
 /*
  * Calibration maxima and SmoothQuant factors ([WAQ] s3 "Choosing the Smoothing Factor").
@@ -72,8 +81,8 @@ w8a8_status w8a8_smooth_scales(const void* x, w8a8_dtype x_dtype, int64_t M, int
                                float* ax, float* aw, int accumulate, float* s, hipStream_t stream);
 
 /*
- * Weight fold and quantize ([WAQ] s3 step 1 "W_tilde = diag(s) @ W" and step 2
- * "W_int8 = quantize(W_tilde)"; per-output-channel scales [ACT]; FP8 per [WAQ] s4).
+ * Weight fold and quantize ([WAQ] s3 step 1, the weight rows scaled by s, and step 2, their
+ * quantization; per-output-channel scales [ACT]; FP8 per [WAQ] s4).
  *   W~[j, n]   = s[j] * W[j, n]                               (fp32 multiply; s == NULL: s = 1)
  *   w_scale[n] = max_j |W~[j, n]| / Q                         (Q = 127 for INT8, 448 for E4M3)
  *   wq[n, j]   = INT8: clamp(round_half_even(W~[j, n] / w_scale[n]), -127, 127)
@@ -86,8 +95,8 @@ w8a8_status w8a8_fold_quant_weight(const void* w, w8a8_dtype w_dtype, int64_t K,
                                    hipStream_t stream);
 
 /*
- * Activation smooth + per-token quantize, one pass over X ([WAQ] s3 "divide each activation
- * channel by s_j" and step 2 "X_int8 = quantize(X_tilde)"; per-token scales [ACT]; FP8 [WAQ] s4).
+ * Activation smooth + per-token quantize, one pass over X ([WAQ] s3: activation channel j
+ * divided by s_j, and step 2, its quantization at inference; per-token scales [ACT]; FP8 [WAQ] s4).
  *   X~[i, j]   = X[i, j] / s[j]                               (fp32 division; s == NULL: s = 1)
  *   x_scale[i] = max_j |X~[i, j]| / Q                         (Q = 127 or 448)
  *   xq[i, j]   = the same rounding as w8a8_fold_quant_weight, with x_scale[i].
@@ -113,10 +122,11 @@ w8a8_status w8a8_smooth_quant(const void* x, w8a8_dtype x_dtype, int64_t M, int6
                               float* w_scale, void* xq, float* x_scale, hipStream_t stream);
 
 /*
- * Quantized GEMM with the dequantizing epilogue ([WAQ] s3 "Y = dequantize(X_int8 @ W_int8)";
+ * Quantized GEMM with the dequantizing epilogue ([WAQ] s3 step 2, the 8-bit product dequantized;
  * [WAQ] s4 x^ = s q for E4M3).
  *   INT8: acc[i, n] = sum_k xq[i, k] * wq[n, k] exactly in int32 (|acc| <= K * 127^2, so
- *         K <= 133144), y[i, n] = bf16(((float)acc * x_scale[i]) * w_scale[n]).
+ *         K <= 133144; codes must lie in [-127, 127], as the quantize calls write them: a -128
+ *         code can overflow the sum at the largest K), y[i, n] = bf16(((float)acc * x_scale[i]) * w_scale[n]).
  *   E4M3: acc = sum_k e4m3(xq[i, k]) * e4m3(wq[n, k]) accumulated in fp32 on the matrix cores
  *         (products are exact; the summation order is the hardware's), y as above.
  * xq: [M, K] bytes, x_scale: fp32 [M], wq: [N, K] bytes, w_scale: fp32 [N], y: bf16 [M, N].
@@ -128,7 +138,7 @@ w8a8_status w8a8_gemm_dequant(const void* xq, const float* x_scale, const void* 
 /*
  * The INT8 GEMM without the epilogue: acc[i, n] = sum_k xq[i, k] * wq[n, k] in int32 [M, N].
  * Same kernels and tiling as w8a8_gemm_dequant; exists so the integer accumulators can be
- * checked bit for bit.  K <= 133144.
+ * checked bit for bit.  K <= 133144, codes in [-127, 127] (as for w8a8_gemm_dequant).
  */
 w8a8_status w8a8_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t M, int64_t N, int64_t K,
                           int32_t* acc, hipStream_t stream);
@@ -143,7 +153,7 @@ w8a8_status w8a8_gemm_f32(const uint8_t* xq, const uint8_t* wq, int64_t M, int64
 
 /*
  * ---- Per-tensor scaling ([WAQ] s4 "Per-Tensor Scaling for FP8": one scale s = max|x| / 448 for a
- * whole tensor, q = cast_fp8(x / s), x^ = s q, no smoothing; the FP8-vs-INT8 table there names
+ * whole tensor, codes of x / s, x^ = s q, no smoothing; the FP8-vs-INT8 table there names
  * delayed scaling, where s comes from the previous step's maximum.  [WAQ] s2 shows the same
  * recipe for INT8 with 127.)  Every scale and maximum below is ONE fp32 value in device memory.
  */

@@ -30,9 +30,10 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
+    path = os.environ.get("W8A8_ORACLE_LIB", LIB_PATH)     # another build of the same source (sanitized)
+    if path == LIB_PATH and not os.path.exists(LIB_PATH):
         build()
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     D, F = ctypes.c_double, ctypes.c_float
     sig = {

@@ -16,14 +16,20 @@ CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contrac
           "-frounding-math", "-fopenmp", "-Wall", "-Wextra"]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
-    cmd = ["gcc", *CFLAGS, SRC, "-o", tmp, "-lm"]
+# Address and undefined-behaviour sanitizers, for the sanitized test build (build(path, SANITIZE)).
+SANITIZE = ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+
+
+def build(verbose: bool = False, path: str | None = None, extra=()) -> str:
+    """Compile the oracle into path (default LIB_PATH) with CFLAGS plus extra."""
+    out = LIB_PATH if path is None else path
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = ["gcc", *CFLAGS, *extra, SRC, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -13,13 +13,13 @@
  *                                                    channel j by s_j, multiply weight channel j
  *                                                    by s_j; two-step pipeline; s_j formula
  *            s4 "FP8 W8A8"                          - E4M3 for weights/activations, range +-448,
- *                                                    q = cast_fp8(x / s), s = max|x| / 448
+ *                                                    codes round x / scale to E4M3, scale = max|x| / 448
  *   [ACT]  "Define activation quantization..." (zenaique flashcard) - per-token / per-channel
  *            scaling of activations and weights.
  *
  * Readings where the pages leave a step open (each is listed with its reason in the design notes):
- *   - division is IEEE fp32 division, not a multiply by a reciprocal ("divide each activation
- *     channel by s_j");
+ *   - division is IEEE fp32 division, not a multiply by a reciprocal (the page divides the activation
+ *     channels by their factors);
  *   - the rounding of quantize() is round-half-to-even; INT8 codes are clamped to [-127, 127];
  *   - X gets one scale per row (token), W~ one scale per output channel (column of W [K, N]);
  *   - "channel j" of s_j is the contraction index: column j of X, row j of W [K, N];
@@ -236,7 +236,7 @@ int oracle_fold_quant_weight(const void* w, int dtype, int64_t K, int64_t N, con
 }
 
 /* ---------------------------------------------------------------------------------------------
- * INT8 GEMM ([WAQ] s3 step 2: Y = dequantize(X_int8 @ W_int8)):
+ * INT8 GEMM ([WAQ] s3 step 2: the product of the two code matrices, then dequantized):
  *   acc[m, n] = sum_k qx[m, k] * qw[n, k], exact in integers.
  * With |codes| <= 127, |acc| <= K * 127^2, which fits int32 for K <= 133144; the sum is kept
  * in int64 and the function returns -1 if any result would not fit int32.
@@ -320,7 +320,7 @@ int oracle_gemm_fp8(const uint8_t* qx, const uint8_t* qw, int64_t M, int64_t N, 
 }
 
 /* ---------------------------------------------------------------------------------------------
- * Per-tensor scaling ([WAQ] s4 "Per-Tensor Scaling for FP8": q = cast_fp8(x / s), x^ = s q with
+ * Per-tensor scaling ([WAQ] s4 "Per-Tensor Scaling for FP8": codes of x / s in E4M3, x^ = s q with
  * s = max|x| / 448; [WAQ] s2 gives the same per-tensor recipe for INT8 with 127).  One scale
  * serves a whole tensor.  Under delayed scaling ([WAQ] s4, the FP8-vs-INT8 table: the scale comes
  * from the previous step's maximum) the maximum is an earlier tensor's, so values beyond Q * s

@@ -450,3 +450,86 @@ def test_int8_largest_k(f, M):
     y = host(f.w8a8_gemm_dequant(xa, dev(sx), wb, dev(sw), "int8"))
     _, yb = oracle.dequant_i32(ref, sx, sw)
     np.testing.assert_array_equal(y, yb)
+
+
+def division_rows(K, rows_per_col, seed):
+    """(X, s) for the division check.  s: one smoothing factor per column, 2^-24 .. 2^24 in
+    magnitude (most inside the fast range [2^-20, 2^20]).  Row m holds a single nonzero
+    X[m, m % K] = t_m * s_(m % K) (rounded to float32), where the target quotient t_m is
+    - random over 2^-100 .. 2^60 (a quarter of the rows),
+    - within two 2^-40 steps of a midpoint between two floats (a quarter),
+    - in the subnormal range 2^-142 .. 2^-126, in columns with s >= 2^-10, so that the row scale
+      |X / s| / Q is a nonzero subnormal (a quarter),
+    - random over 2^-60 .. 2^20 (the rest)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    M = K * rows_per_col
+    s = np.ldexp(rng.uniform(1, 2, K), rng.integers(-24, 25, K)).astype(np.float32)
+    col = np.arange(M) % K
+    sign = rng.choice([-1.0, 1.0], M)
+    t = np.ldexp(rng.uniform(1, 2, M), rng.integers(-60, 21, M))
+    k = M // 4
+    t[:k] = np.ldexp(rng.uniform(1, 2, k), rng.integers(-100, 61, k))
+    q = np.ldexp(rng.uniform(1, 2, k), rng.integers(-40, 41, k)).astype(np.float32).astype(np.float64)
+    t[k:2 * k] = (q + np.ldexp(1.0, np.frexp(q)[1] - 25)) * (1 + rng.integers(-2, 3, k) * 2.0 ** -40)
+    sub = np.arange(2 * k, 3 * k)
+    sub = sub[s[col[sub]] >= 2.0 ** -10]
+    t[sub] = np.ldexp(rng.uniform(1, 2, len(sub)), rng.integers(-142, -126, len(sub)))
+    X = np.zeros((M, K), np.float32)
+    X[np.arange(M), col] = (sign * t * s[col].astype(np.float64)).astype(np.float32)
+    return X, s
+
+
+@pytest.mark.parametrize("qtype", ["int8", "fp8"])
+def test_division_through_row_scales(f, qtype):
+    """X / s checked one quotient at a time: row m holds one nonzero X[m, m % K], divided by
+    s[m % K], so x_scale[m] = |X / s| / Q exposes the rounding of that one division (subnormal
+    quotients included).  Codes and scales against the oracle's IEEE divisions, bit for bit."""
+    K, rows_per_col = 4096, 16
+    announce(f"division through row scales {qtype} M={K * rows_per_col} K={K}")
+    X, s = division_rows(K, rows_per_col, 91)
+    assert np.isfinite(X).all()
+    xq, sx = f.w8a8_quant_act(dev(X), dev(s), qtype)
+    xq, sx = host(xq), host(sx)
+    qx_ref, sx_ref = oracle.quant_act(X, s, qtype)
+    np.testing.assert_array_equal(sx, sx_ref)
+    np.testing.assert_array_equal(xq.view(np.uint8), qx_ref.view(np.uint8))
+    assert np.count_nonzero((sx_ref > 0) & (sx_ref < np.float32(2.0 ** -126))) > 1000   # subnormal scales occur
+
+
+def test_repeat_calls_are_bit_identical(f):
+    """Every kernel family run twice on the same normal inputs gives the same bits: the one-call
+    preparation (its maxima merge with order-free atomics), the activation quantize, the INT8 and
+    E4M3 GEMMs (tiled and small-M), the RMS norm and LayerNorm quantize and the W8A16 GEMM."""
+    announce("determinism")
+    X = synth.random_matrix((1000, 2048), 95, "bf16", outliers=20)
+    W = synth.random_matrix((2048, 1536), 96, "bf16", scale=0.02)
+    x, w = dev(X), dev(W)
+    outs = []
+    for _ in range(2):
+        r = {}
+        for qt in ("int8", "fp8"):
+            p = f.w8a8_smooth_quant(x, w, 0.5, qt)
+            r[qt] = {k: host(v) for k, v in p.items()}
+            r[qt + "_act"] = host(f.w8a8_quant_act(x, p["s"], qt)[0])
+            r[qt + "_y"] = host(f.w8a8_gemm_dequant(p["xq"], p["x_scale"], p["wq"], p["w_scale"], qt))
+            r[qt + "_y8"] = host(f.w8a8_gemm_dequant(p["xq"][:8].contiguous(), p["x_scale"][:8].contiguous(),
+                                                     p["wq"], p["w_scale"], qt))
+            g = f.w8a8_fold_norm_gain(None, p["s"])
+            r[qt + "_rms"] = [host(t) for t in f.w8a8_norm_quant_act(x, g, 1e-5, qt)]
+            r[qt + "_ln"] = [host(t) for t in f.w8a8_layer_norm_quant_act(x, g, g, 1e-5, qt)]
+        wq, sw = f.w8a8_fold_quant_weight(w, None, "int8")
+        r["w8a16"] = host(f.w8a8_gemm_w8a16(x, wq, sw))
+        torch.cuda.synchronize()
+        outs.append(r)
+
+    def same(u, v, path):
+        if isinstance(u, dict):
+            for k in u:
+                same(u[k], v[k], f"{path}.{k}")
+        elif isinstance(u, list):
+            for i, (p, q) in enumerate(zip(u, v)):
+                same(p, q, f"{path}[{i}]")
+        else:
+            assert u.tobytes() == v.tobytes(), path
+
+    same(outs[0], outs[1], "run")

@@ -36,7 +36,7 @@ def int8_ref(v, scale):
 
 
 def e4m3_ref(v, scale):
-    """torch's E4M3 cast of the fp32 quotient clamped to +-448 (the s4 cast_fp8(x / s))."""
+    """torch's E4M3 cast of the fp32 quotient clamped to +-448 (the section 4 conversion of x / s)."""
     with np.errstate(over="ignore"):
         t = (f32(v) / np.float32(scale)).astype(np.float32)
     t = np.clip(t, -448, 448)
