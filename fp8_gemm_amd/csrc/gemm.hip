@@ -183,9 +183,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Written as inline asm rather than the compiler's LDS-DMA builtin: the compiler cannot tell which
 // stage a DMA writes, so before any LDS read that follows one it waits for every copy in flight,
 // which would empty the pipeline each half step.  Here the waits are explicit (wait_copies).  The
-// asm sets M0 (the LDS destination of the DMA); the compiler reserves M0 and warns about the
-// clobber, and these kernels use M0 for nothing else (their gfx950 assembly holds no other write or
-// read of it), so the warning is silenced for these two functions.
+// asm sets M0 (the LDS destination of the DMA).  The compiler reserves M0 and does not preserve it
+// around asm, so these kernels must use M0 for nothing else: tests/test_codegen.py compiles this
+// file and checks that every write of M0 in the GEMM kernels is this sequence and that no other
+// instruction writes or (implicitly) reads it.  The compiler's warning about the clobber is
+// silenced for these two functions.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void copy_sv(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
