@@ -196,6 +196,29 @@ def w8a8_smooth_quant(x, w, alpha: float = 0.5, qtype="int8", out=None, stream=N
     return out
 
 
+def w8a8_quant_pair(x, w, s, w_scale, qtype="int8", xq=None, x_scale=None, wq=None, stream=None):
+    """Both operands' codes in one launch, given s [K] and the final weight scales w_scale [N]
+    (those of w8a8_fold_quant_weight / w8a8_smooth_quant): returns (xq [M, K], x_scale [M],
+    wq [N, K])."""
+    _, M, K = _mat(x, "x", _FLOAT_IN)
+    _, K2, N = _mat(w, "w", _FLOAT_IN)
+    if K2 != K:
+        raise ValueError("x is [M, K] and w is [K, N]")
+    if s is None or w_scale is None:
+        raise ValueError("w8a8_quant_pair needs s and w_scale")
+    _arg(s, "s", _F32, K)
+    _arg(w_scale, "w_scale", _F32, N)
+    q = _qtype(qtype)
+    codes = (_code_dtype(q),) + _CODES
+    xq = _out(xq, "xq", codes, (M, K), x.device)
+    x_scale = _out(x_scale, "x_scale", _F32, M, x.device)
+    wq = _out(wq, "wq", codes, (N, K), x.device)
+    _check("w8a8_quant_pair", _load().w8a8_quant_pair(
+        _ptr(x), _dtype(x), M, K, _ptr(w), _dtype(w), N, _ptr(s), _ptr(w_scale), q, _ptr(xq), _ptr(x_scale),
+        _ptr(wq), _stream(stream)))
+    return xq, x_scale, wq
+
+
 def _gemm_operands(xq, wq):
     _, M, K = _mat(xq, "xq", _CODES)
     _, N, K2 = _mat(wq, "wq", _CODES)

@@ -16,6 +16,7 @@ SIGNATURES = {
     "w8a8_fold_quant_weight": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _P, _P]),
     "w8a8_quant_act": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _P, _P]),
     "w8a8_smooth_quant": (_I, [_P, _I, _I64, _I64, _P, _I, _I64, _F, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "w8a8_quant_pair": (_I, [_P, _I, _I64, _I64, _P, _I, _I64, _P, _P, _I, _P, _P, _P, _P]),
     "w8a8_gemm_dequant": (_I, [_P, _P, _P, _P, _I, _I64, _I64, _I64, _P, _P]),
     "w8a8_gemm_i32": (_I, [_P, _P, _I64, _I64, _I64, _P, _P]),
     "w8a8_gemm_f32": (_I, [_P, _P, _I64, _I64, _I64, _P, _P]),

@@ -120,6 +120,35 @@ W8A8_API w8a8_status w8a8_quant_act(const void* x, w8a8_dtype x_dtype, int64_t M
                                            static_cast<uint8_t*>(xq), x_scale, stream));
 }
 
+W8A8_API w8a8_status w8a8_quant_pair(const void* x, w8a8_dtype x_dtype, int64_t M, int64_t K, const void* w,
+                                     w8a8_dtype w_dtype, int64_t N, const float* s, const float* w_scale,
+                                     w8a8_qtype qtype, void* xq, float* x_scale, void* wq, hipStream_t stream) {
+    if (!valid_dtype(x_dtype) || !valid_dtype(w_dtype) || !valid_qtype(qtype) || !s) return W8A8_ERR_INVALID_ARG;
+    if (M > 0 && (!x || !xq || !x_scale)) return W8A8_ERR_INVALID_ARG;
+    if (N > 0 && (!w || !wq || !w_scale)) return W8A8_ERR_INVALID_ARG;
+    w8a8_status st = check_dims(M, N, K);
+    if (st != W8A8_OK) return st;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(s) || !aligned16(w_scale) || !aligned16(xq) ||
+        !aligned16(x_scale) || !aligned16(wq))
+        return W8A8_ERR_UNSUPPORTED;
+    const bool fp8 = qtype == W8A8_FP8_E4M3;
+    const bool one_launch = x_dtype == w_dtype && M >= 1 && N >= 1 && N % 8 == 0 && K <= 8192 &&
+                            M < (int64_t(1) << 23) && N < (int64_t(1) << 23);
+    hipError_t e = hipSuccess;
+    if (one_launch) {
+        e = w8a8::launch_quant_pair(x, x_dtype == W8A8_BF16, M, K, s, fp8, static_cast<uint8_t*>(xq), x_scale, w, N,
+                                    w_scale, static_cast<uint8_t*>(wq), stream);
+    } else {
+        if (M > 0)
+            e = w8a8::launch_quant_act(x, x_dtype == W8A8_BF16, M, K, s, fp8, static_cast<uint8_t*>(xq), x_scale,
+                                       stream);
+        if (e == hipSuccess && N > 0)
+            e = w8a8::launch_quant_weight_t(w, w_dtype == W8A8_BF16, K, N, s, w_scale, false, fp8,
+                                            static_cast<uint8_t*>(wq), stream);
+    }
+    return from_hip(e);
+}
+
 W8A8_API w8a8_status w8a8_gemm_dequant(const void* xq, const float* x_scale, const void* wq, const float* w_scale,
                                        w8a8_qtype qtype, int64_t M, int64_t N, int64_t K, void* y,
                                        hipStream_t stream) {

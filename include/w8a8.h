@@ -122,6 +122,23 @@ w8a8_status w8a8_smooth_quant(const void* x, w8a8_dtype x_dtype, int64_t M, int6
                               float* w_scale, void* xq, float* x_scale, hipStream_t stream);
 
 /*
+ * The codes of both operands in one launch, given the smoothing factors and the final weight
+ * scales: the last step of w8a8_smooth_quant, for callers that hold s and w_scale already ([WAQ]
+ * s3 step 2 for X, the quantization of the smoothed weights for W; scales per token and per output
+ * channel [ACT]; FP8 [WAQ] s4).
+ *   xq, x_scale: exactly as w8a8_quant_act(x, s) writes them;
+ *   wq:          the codes of w8a8_fold_quant_weight(w, s) with the given w_scale, which must be
+ *                the scales that call (or w8a8_smooth_quant) computes, max_j |s[j] W[j, n]| / Q.
+ * x: [M, K], w: [K, N]; s: fp32 [K] (not NULL); w_scale: fp32 [N] (read only); xq [M, K], x_scale
+ * [M], wq [N, K] written; none may overlap x, w, s or w_scale.  X and W of one dtype, N % 8 == 0
+ * and K <= 8192 take one launch, other shapes two (the activation quantize, then the weight codes).
+ * M or N may be 0 (that operand is skipped).  Errors as w8a8_quant_act and w8a8_fold_quant_weight.
+ */
+w8a8_status w8a8_quant_pair(const void* x, w8a8_dtype x_dtype, int64_t M, int64_t K, const void* w,
+                            w8a8_dtype w_dtype, int64_t N, const float* s, const float* w_scale,
+                            w8a8_qtype qtype, void* xq, float* x_scale, void* wq, hipStream_t stream);
+
+/*
  * Quantized GEMM with the dequantizing epilogue ([WAQ] s3 step 2, the 8-bit product dequantized;
  * [WAQ] s4 x^ = s q for E4M3).
  *   INT8: acc[i, n] = sum_k xq[i, k] * wq[n, k] exactly in int32 (|acc| <= K * 127^2, so

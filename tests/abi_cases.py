@@ -52,6 +52,13 @@ def check_argument_validation(L):
                                None) == UNS                                             # K % 16
     assert L.w8a8_smooth_quant(fake, 1, 4, 16, fake, 1, 8, 0.5, 0, fake, fake, fake, odd, fake, fake, fake,
                                None) == UNS                                             # alignment
+    # quant_pair (x, xt, M, K, w, wt, N, s, w_scale, qtype, xq, x_scale, wq, stream)
+    assert L.w8a8_quant_pair(fake, 1, 4, 16, fake, 1, 8, None, fake, 0, fake, fake, fake, None) == INV     # NULL s
+    assert L.w8a8_quant_pair(fake, 1, 4, 16, fake, 1, 8, fake, None, 0, fake, fake, fake, None) == INV     # NULL w_scale
+    assert L.w8a8_quant_pair(fake, 1, 4, 16, fake, 9, 8, fake, fake, 0, fake, fake, fake, None) == INV     # bad dtype
+    assert L.w8a8_quant_pair(fake, 1, 4, 16, fake, 1, 8, fake, fake, 3, fake, fake, fake, None) == INV     # bad qtype
+    assert L.w8a8_quant_pair(fake, 1, 4, 24, fake, 1, 8, fake, fake, 0, fake, fake, fake, None) == UNS     # K % 16
+    assert L.w8a8_quant_pair(fake, 1, 4, 16, fake, 1, 8, fake, fake, 0, fake, fake, odd, None) == UNS      # alignment
     # fold
     assert L.w8a8_fold_quant_weight(None, 1, 16, 8, None, 0, fake, fake, None) == INV
     assert L.w8a8_fold_quant_weight(fake, 1, 16, 0, None, 0, None, None, None) == OK

@@ -147,3 +147,38 @@ def test_smooth_quant_large_workloads(f, name):
     announce(f"smooth_quant {wl.name}")
     X, W = synth.make_inputs(wl, seed=0)
     check(f, X, W, wl.alpha, wl.qtype)
+
+
+@pytest.mark.parametrize("qtype", ["int8", "fp8"])
+@pytest.mark.parametrize("M,K,N,xdt,wdt", [(70, 1040, 136, "bf16", "bf16"), (129, 4096, 264, "f32", "f32"),
+                                          (2048, 4096, 4096, "bf16", "bf16"), (16, 4096, 14336, "bf16", "bf16"),
+                                          (33, 512, 100, "bf16", "bf16"),        # N % 8 != 0: two launches
+                                          (40, 8208, 64, "bf16", "bf16"),        # K > 8192: two launches
+                                          (24, 256, 48, "f32", "bf16")])         # mixed dtypes: two launches
+def test_quant_pair(f, qtype, M, K, N, xdt, wdt):
+    """w8a8_quant_pair given the oracle's s and weight scales: both operands' codes and the token
+    scales bit-exact against the oracle, in one launch or two."""
+    announce(f"quant_pair {qtype} M={M} K={K} N={N} {xdt}/{wdt}")
+    X, W = inputs(M, K, N, xdt, wdt, 31)
+    ax, aw, s = oracle.smooth_scales(X, W, 0.5)
+    qw, sw = oracle.fold_quant_weight(W, s, qtype)
+    qx, sx = oracle.quant_act(X, s, qtype)
+    xq, x_scale, wq = f.w8a8_quant_pair(dev(X), dev(W), dev(s), dev(sw), qtype)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(x_scale), sx)
+    np.testing.assert_array_equal(codes(host(xq)), codes(qx))
+    np.testing.assert_array_equal(codes(host(wq)), codes(qw))
+
+
+def test_quant_pair_empty_operand(f):
+    """M = 0 writes only the weight codes; N = 0 only the activation codes."""
+    X, W = inputs(20, 256, 64, "bf16", "bf16", 33)
+    ax, aw, s = oracle.smooth_scales(X, W, 0.5)
+    qw, sw = oracle.fold_quant_weight(W, s, "int8")
+    qx, sx = oracle.quant_act(X, s, "int8")
+    xq, x_scale, wq = f.w8a8_quant_pair(dev(X[:0]), dev(W), dev(s), dev(sw), "int8")
+    np.testing.assert_array_equal(codes(host(wq)), codes(qw))
+    xq, x_scale, wq = f.w8a8_quant_pair(dev(X), dev(W[:, :0]), dev(s), dev(sw[:0]), "int8")
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(codes(host(xq)), codes(qx))
+    np.testing.assert_array_equal(host(x_scale), sx)
