@@ -28,6 +28,7 @@ namespace w8a8 {
 
 namespace {
 
+
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 constexpr int kChunk = 64;              // k per chunk: two instructions
 constexpr int kThreads16 = 256;         // 4 waves
@@ -157,11 +158,11 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void w8a16_decode_kernel(const u
 }
 
 // ------------------------------------------------------------------------------------------------
-// General kernel (any M, any K): a block owns 16 output columns and 16 kMT rows; its 4 waves take
+// Small-M kernel (any K): a block owns 16 output columns and 16 kMT rows; its 4 waves take
 // contiguous ranges of 64-wide K chunks, load both operands straight from global memory, and add
 // their partial sums in LDS.  The k of a partial last chunk past K (K % 64 = 16, 32 or 48: whole
-// 16-k pieces) use zero operands.  It is a correct general path, not a fast one past a few rows:
-// without LDS tiling every 16-row fragment comes from L2 (about 140 TFLOP/s at M = 4096).
+// 16-k pieces) use zero operands.  Without LDS tiling every 16-row fragment comes from L2, so it
+// serves only a few rows (up to 128), where its N / 16 blocks keep the chip busy.
 // ------------------------------------------------------------------------------------------------
 template <int kMT>
 __global__ __launch_bounds__(kThreads16) void w8a16_kernel(const uint16_t* __restrict__ x,
@@ -250,6 +251,160 @@ __global__ __launch_bounds__(kThreads16) void w8a16_kernel(const uint16_t* __res
     }
 }
 
+// ------------------------------------------------------------------------------------------------
+// Tiled kernel (batches past the decode shape): a block owns a kBM x kBN output tile; its 4 waves in
+// a 2 x 2 grid own (kBM / 2) x (kBN / 2) each, as 32 x 32 blocks of v_mfma_f32_32x32x16_bf16 (A = 32
+// output channels of W, B = 32 rows of X; lane l supplies row l % 32 and 8 k of each operand).
+// K is taken 32 at a time.  Both operands go through LDS as bf16: the W codes are converted once,
+// while staged, so each W element is converted once per block and both tiles share one layout:
+// 64 bytes per row and K step, as four 16-byte chunks; chunk c of row r is stored at chunk
+// c ^ ((r >> 2) & 3), which makes the 16-lane phases of a fragment read (16 rows at one chunk)
+// hit 16 different 16-byte bank groups.  Two LDS stages and two register sets for the global
+// loads: the loads of step t + 2 go out when step t starts, and step t + 1's (loaded during step
+// t - 1) are written to LDS when step t ends, so each load has two steps to land.  Rows past M or
+// N re-read the last row (never stored); the k past K (K % 32 = 16) are zero.
+// ------------------------------------------------------------------------------------------------
+typedef float v16f __attribute__((ext_vector_type(16)));
+constexpr int kKS = 32;                  // k per step
+constexpr int kRowBytes = kKS * 2;       // bytes per row and step (bf16)
+
+__device__ __forceinline__ int tswz(int row, int chunk) { return row * kRowBytes + ((chunk ^ ((row >> 2) & 3)) << 4); }
+
+template <int kBM, int kBN>
+__global__ __launch_bounds__(256, 2) void w8a16_tile_kernel(const uint16_t* __restrict__ x, const int8_t* __restrict__ wq,
+                                                            const float* __restrict__ w_scale, int64_t M, int64_t N,
+                                                            int64_t K, uint16_t* __restrict__ y, int tiles_m,
+                                                            int tiles_n) {
+    constexpr int kMT = kBM / 64, kNT = kBN / 64;           // 32 x 32 blocks per wave along M and N
+    constexpr int kXChunks = kBM * 4, kWChunks = kBN * 2;  // 16-byte X chunks, 16-code W chunks per step
+    constexpr int kThreads = 256;
+    constexpr int kXPer = (kXChunks + kThreads - 1) / kThreads, kWPer = (kWChunks + kThreads - 1) / kThreads;
+    constexpr int kXStage = kBM * kRowBytes, kWStage = kBN * kRowBytes;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (kXStage + kWStage)];
+    uint8_t* const xs = smem;
+    uint8_t* const ws = smem + 2 * kXStage;
+
+    // XCD-aware order: consecutive block ids go to the 8 XCDs in turn; give each XCD a contiguous
+    // range of tiles, walked 4 tile rows at a time, so the blocks sharing an L2 share operands.
+    int bid = blockIdx.x;
+    const int nblocks = gridDim.x, full = (nblocks / 8) * 8;
+    if (bid < full) bid = (bid % 8) * (full / 8) + bid / 8;
+    constexpr int kGroupM = 4;
+    const int g = bid / (kGroupM * tiles_n), first = g * kGroupM;
+    const int gm = min(tiles_m - first, kGroupM);
+    const int in = bid % (kGroupM * tiles_n);
+    const int64_t m0 = static_cast<int64_t>(first + in % gm) * kBM, n0 = static_cast<int64_t>(in / gm) * kBN;
+
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int wm = wave / 2, wn = wave % 2;
+    const int r32 = lane % 32, g32 = lane / 32;
+
+    // Staging: X chunk p = tid + 256 i is row p / 4, chunk p % 4 (8 bf16); W chunk p = tid + 256 i
+    // is row p / 2, half p % 2 (16 codes, two bf16 chunks).
+    const uint16_t* xsrc[kXPer];
+    int xl[kXPer], xk[kXPer];
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) {
+        const int p = min(static_cast<int>(threadIdx.x) + kThreads * i, kXChunks - 1), row = p / 4, c = p % 4;
+        const int64_t gr = min(m0 + row, M - 1);
+        xsrc[i] = x + gr * K + c * 8;
+        xl[i] = tswz(row, c);
+        xk[i] = c * 8;
+    }
+    const int8_t* wsrc[kWPer];
+    int wl[kWPer], wk[kWPer];
+#pragma unroll
+    for (int i = 0; i < kWPer; ++i) {
+        const int p = min(static_cast<int>(threadIdx.x) + kThreads * i, kWChunks - 1), row = p / 2, h = p % 2;
+        const int64_t gr = min(n0 + row, N - 1);
+        wsrc[i] = wq + gr * K + h * 16;
+        wl[i] = row;
+        wk[i] = h * 16;
+    }
+    uint4 xr[2][kXPer], wr[2][kWPer];
+    auto load = [&](int set, int t) {
+        const int64_t k0 = static_cast<int64_t>(t) * kKS;
+#pragma unroll
+        for (int i = 0; i < kXPer; ++i)
+            xr[set][i] = k0 + xk[i] < K ? *reinterpret_cast<const uint4*>(xsrc[i] + k0) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int i = 0; i < kWPer; ++i)
+            wr[set][i] = k0 + wk[i] < K ? *reinterpret_cast<const uint4*>(wsrc[i] + k0) : make_uint4(0u, 0u, 0u, 0u);
+    };
+    // Threads past the chunk count (small tiles) load a duplicate of the last chunk and store nothing.
+    auto store = [&](int set, int stage) {
+#pragma unroll
+        for (int i = 0; i < kXPer; ++i)
+            if (threadIdx.x + kThreads * i < kXChunks) *reinterpret_cast<uint4*>(xs + stage * kXStage + xl[i]) = xr[set][i];
+#pragma unroll
+        for (int i = 0; i < kWPer; ++i) {
+            if (threadIdx.x + kThreads * i >= kWChunks) continue;
+            const int c0 = 2 * (wk[i] / 16);
+            *reinterpret_cast<v8bf*>(ws + stage * kWStage + tswz(wl[i], c0)) =
+                codes_to_bf16(make_uint2(wr[set][i].x, wr[set][i].y));
+            *reinterpret_cast<v8bf*>(ws + stage * kWStage + tswz(wl[i], c0 + 1)) =
+                codes_to_bf16(make_uint2(wr[set][i].z, wr[set][i].w));
+        }
+    };
+
+    v16f acc[kMT][kNT];
+#pragma unroll
+    for (int i = 0; i < kMT; ++i)
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) acc[i][j] = v16f{};
+
+    const int nk = static_cast<int>((K + kKS - 1) / kKS);
+    // Register set t % 2 holds the loads of step t; LDS stage t % 2 the tile of step t.
+    load(0, 0);
+    if (nk > 1) load(1, 1);
+    store(0, 0);
+    __syncthreads();
+    auto step = [&](int t, auto SET) {
+        constexpr int set = decltype(SET)::value;   // t % 2, known at compile time
+        const int stage = set;
+        if (t + 2 < nk) load(set, t + 2);           // set t % 2 was stored at the end of step t - 1
+        // instruction u of the step takes k 16 u .. 16 u + 15: lane group g32 supplies chunk 2 u + g32
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            v8bf fx[kMT], fw[kNT];
+#pragma unroll
+            for (int i = 0; i < kMT; ++i)
+                fx[i] = *reinterpret_cast<const v8bf*>(xs + stage * kXStage + tswz(wm * (kBM / 2) + 32 * i + r32, 2 * u + g32));
+#pragma unroll
+            for (int j = 0; j < kNT; ++j)
+                fw[j] = *reinterpret_cast<const v8bf*>(ws + stage * kWStage + tswz(wn * (kBN / 2) + 32 * j + r32, 2 * u + g32));
+#pragma unroll
+            for (int i = 0; i < kMT; ++i)
+#pragma unroll
+                for (int j = 0; j < kNT; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[j], fx[i], acc[i][j], 0, 0, 0);
+        }
+        if (t + 1 < nk) store(set ^ 1, stage ^ 1);   // step t + 1's loads; that stage was last read in step t - 1
+        __syncthreads();
+    };
+    int t = 0;
+    for (; t + 1 < nk; t += 2) {
+        step(t, std::integral_constant<int, 0>{});
+        step(t + 1, std::integral_constant<int, 1>{});
+    }
+    if (t < nk) step(t, std::integral_constant<int, 0>{});
+    // Lane results of block (i, j): row m = m0 + wm (kBM / 2) + 32 i + r32, columns
+    // n = n0 + wn (kBN / 2) + 32 j + 8 q + 4 g32 + r (r = 0..3) in acc[4 q + r].
+#pragma unroll
+    for (int j = 0; j < kNT; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t n = n0 + wn * (kBN / 2) + 32 * j + 8 * q + 4 * g32;
+            const v4f sc = load_scales4(w_scale, n, N);
+#pragma unroll
+            for (int i = 0; i < kMT; ++i) {
+                const int64_t m = m0 + wm * (kBM / 2) + 32 * i + r32;
+                const v4f a = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                store_w8a16(a, sc, m, n, M, N, y);
+            }
+        }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_w8a16(const uint16_t* x, const int8_t* wq, const float* w_scale, int64_t M, int64_t N,
@@ -267,10 +422,23 @@ hipError_t launch_gemm_w8a16(const uint16_t* x, const int8_t* wq, const float* w
     if (M <= 16) {
         hipLaunchKernelGGL((w8a16_kernel<1>), dim3(static_cast<unsigned>((N + 15) / 16), 1), dim3(kThreads16), 0, st, x,
                            wq, w_scale, M, N, K, y);
-    } else {
+        return hipGetLastError();
+    }
+    if (M <= 128 && M * N <= 128 * 4096) {
+        // Few rows: the untiled kernel's N / 16 blocks fill the chip, where the tiled kernel has a
+        // few dozen tiles each walking all of K (measured: 20.6 against 51 us at M = 64, N = 4096).
         hipLaunchKernelGGL((w8a16_kernel<4>), dim3(static_cast<unsigned>((N + 15) / 16), static_cast<unsigned>((M + 63) / 64)),
                            dim3(kThreads16), 0, st, x, wq, w_scale, M, N, K, y);
+        return hipGetLastError();
     }
+    // Tiled: 128 x 128 tiles when there are enough of them for two per CU, else 64 x 64.
+    auto launch_tiled = [&](auto kernel, int bm, int bn) {
+        const int tm = static_cast<int>((M + bm - 1) / bm), tn = static_cast<int>((N + bn - 1) / bn);
+        hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(tm * tn)), dim3(256), 0, st, x, wq, w_scale, M, N, K, y,
+                           tm, tn);
+    };
+    if (((M + 127) / 128) * ((N + 127) / 128) >= 512) launch_tiled(w8a16_tile_kernel<128, 128>, 128, 128);
+    else launch_tiled(w8a16_tile_kernel<64, 64>, 64, 64);
     return hipGetLastError();
 }
 

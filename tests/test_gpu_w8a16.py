@@ -8,8 +8,9 @@ Bar:
   - real bf16 X: within 1e-2 relative of the oracle's double-precision value plus the worst-case
     accumulation error of the matrix cores (gpu_util.fp8_accumulation_bound, which also covers an
     fp32 accumulation of exact products).
-Shapes cover the decode kernel (M <= 16, K = 4096) and the general kernel (1 and 4 row blocks,
-ragged M and N, a K that ends in half a step).
+Shapes cover the decode kernel (M <= 16, K = 4096), the small-M kernel (up to 128 rows on narrow
+layers), and the tiled kernel with 64 x 64 and 128 x 128 tiles (ragged M and N, fewer rows than
+one tile, a K that ends in half a 32-wide step, a grid that does not divide into the 8 XCDs).
 """
 import numpy as np
 import pytest
@@ -33,7 +34,8 @@ def f():
 
 # (M, K, N): decode kernel; general kernel with one row block, with four, several row blocks
 SHAPES = [(1, 4096, 1000), (7, 4096, 4100), (16, 4096, 96), (5, 528, 77), (40, 1040, 300), (300, 4096, 130),
-          (129, 2064, 517)]
+          (129, 2064, 517), (17, 48, 33), (100, 528, 8200), (1000, 1040, 1000), (2050, 272, 4100),
+          (4096, 4096, 4096)]
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
