@@ -87,20 +87,21 @@ __device__ __forceinline__ int out_col(int lane, int g) {
 
 // Dequantize and store four consecutive outputs of row m starting at column n (or store the raw
 // accumulators when kOutAcc).  tensor: one scale for all of W (w_scale[0]) instead of one per column.
+// Columns at or past ncap (<= N) are not stored.
 template <bool kOutAcc, typename T>
 __device__ __forceinline__ void store4(const T (&a)[4], int64_t m, int64_t n, int64_t M, int64_t N, float sxm,
                                        const float* __restrict__ w_scale, bool tensor, uint16_t* __restrict__ y,
-                                       void* __restrict__ out_acc) {
+                                       void* __restrict__ out_acc, int64_t ncap) {
     if (m >= M) return;
     if constexpr (kOutAcc) {
         T* p = static_cast<T*>(out_acc) + m * N + n;
-        if (n + 3 < N && (N & 3) == 0) {
+        if (n + 3 < ncap && (N & 3) == 0) {
             typedef T v4t __attribute__((ext_vector_type(4)));
             *reinterpret_cast<v4t*>(p) = v4t{a[0], a[1], a[2], a[3]};
         } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                if (n + r < N) p[r] = a[r];
+                if (n + r < ncap) p[r] = a[r];
         }
     } else {
         float v[4];
@@ -111,14 +112,14 @@ __device__ __forceinline__ void store4(const T (&a)[4], int64_t m, int64_t n, in
         }
         const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
         uint16_t* p = y + m * N + n;
-        if (n + 3 < N && (N & 3) == 0) {
+        if (n + 3 < ncap && (N & 3) == 0) {
             *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
         } else {
             const uint16_t h[4] = {static_cast<uint16_t>(lo), static_cast<uint16_t>(lo >> 16),
                                    static_cast<uint16_t>(hi), static_cast<uint16_t>(hi >> 16)};
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                if (n + r < N) p[r] = h[r];
+                if (n + r < ncap) p[r] = h[r];
         }
     }
 }
@@ -129,14 +130,14 @@ template <typename MM, bool kOutAcc>
 __device__ __forceinline__ void store_block(const typename MM::Acc& acc, int64_t m_base, int64_t n_base, int lane,
                                             int64_t M, int64_t N, const float* __restrict__ x_scale,
                                             const float* __restrict__ w_scale, bool tensor,
-                                            uint16_t* __restrict__ y, void* __restrict__ out_acc) {
+                                            uint16_t* __restrict__ y, void* __restrict__ out_acc, int64_t ncap) {
     using T = typename std::remove_cv<typename std::remove_reference<decltype(acc[0])>::type>::type;
     const int64_t m = m_base + out_row<MM::kTile>(lane);
     const float sxm = (!kOutAcc && m < M) ? x_scale[tensor ? 0 : m] : 0.0f;
 #pragma unroll
     for (int g = 0; g < MM::kGroups; ++g) {
         const T a[4] = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
-        store4<kOutAcc>(a, m, n_base + out_col<MM::kTile>(lane, g), M, N, sxm, w_scale, tensor, y, out_acc);
+        store4<kOutAcc>(a, m, n_base + out_col<MM::kTile>(lane, g), M, N, sxm, w_scale, tensor, y, out_acc, ncap);
     }
 }
 
@@ -533,7 +534,7 @@ __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void gemm_til
 #pragma unroll
             for (int j = 0; j < kNT; ++j)
                 store_block<MM, kOutAcc>(acc[i][j], mw0 + i * MM::kTile, nw0 + j * MM::kTile, lane, M, N, x_scale,
-                                         w_scale, tensor_scales != 0, y, out_acc);
+                                         w_scale, tensor_scales != 0, y, out_acc, N);
     } else {
         // Dequantize in registers, stage the wave's kWM x kWN bf16 tile in LDS (rows padded to
         // kOutStride bytes), and write it back as 16-byte pieces of whole output rows.
@@ -659,33 +660,49 @@ __global__ __launch_bounds__(kThreads) void gemm_small_m_kernel(
 #pragma unroll
             for (int w = 0; w < 3; ++w) a += red[w][i][lane];
             store_block<MM, kOutAcc>(a, static_cast<int64_t>(i) * 16, n0, lane, M, N, x_scale, w_scale,
-                                     tensor_scales != 0, y, out_acc);
+                                     tensor_scales != 0, y, out_acc, N);
         }
     }
 }
 
 // ------------------------------------------------------------------------------------------------
-// Decode kernel (M <= 16, K = 4 * kS * kKStep): bound by reading W once.  Each of the 4 waves of a
-// block owns a contiguous quarter of K and holds its X fragments for that quarter in registers for
-// the whole kernel, so X is read once per wave instead of once per output tile.  A block walks the
-// 16-column output tiles t = blockIdx.x, blockIdx.x + gridDim.x, ...: it loads the W fragments of
-// the next tile while the matrix cores work on the current one, then adds the 4 partial sums in LDS
-// (exact for INT8) and the first wave stores them.
+// Decode kernel (M <= 16, K = 8 * kS * kKStep): bound by reading W once.  A block has 8 waves; wave
+// w owns the w-th eighth of K and holds its X fragments for that eighth in registers for the whole
+// kernel, so X is read once per wave instead of once per output tile.  Block b owns the output
+// columns [b cols, (b + 1) cols): cols is a multiple of 8 chosen so that every CU streams the same
+// share of W (at N = 14336, 56 columns: three 16-column tiles and one of 8, whose other 8 rows
+// re-read the last row, from cache, and are not stored).  W fragments of kDepth tiles are in
+// flight per wave (at kDepth = 4 and 8 waves, 256 KB per block: the whole share at N = 14336), and
+// a buffer is refilled as soon as the matrix cores have consumed it.  kDepth is the block's tile
+// count, up to 4 (INT8) or 2 (E4M3, whose fragments are twice as large), so that no buffer is
+// loaded for a tile the block does not have.
+// Each wave writes its partial sums per tile to LDS; after one barrier the partials are added
+// (exact for INT8) and stored, so no store sits between two waits for loads.
 // ------------------------------------------------------------------------------------------------
-template <int kS, typename MM, bool kOutAcc>
-__global__ __launch_bounds__(kThreads) void gemm_decode_kernel(
+constexpr int kDecodeThreads = 512;       // 8 waves
+constexpr int kDecodeMaxTiles = 8;        // columns per block <= 8 tiles of 16
+#ifndef W8A8_DECODE_BLOCKS
+#define W8A8_DECODE_BLOCKS 256
+#endif
+constexpr int kDecodeBlocks = W8A8_DECODE_BLOCKS;   // blocks the columns are spread over
+
+template <int kS, int kDepth, typename MM, bool kOutAcc>
+__global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ x_scale, const uint8_t* __restrict__ wq,
     const float* __restrict__ w_scale, int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y,
-    void* __restrict__ out_acc, int tensor_scales) {
+    void* __restrict__ out_acc, int tensor_scales, int cols) {
     using Acc = typename MM::Acc;
     static_assert(MM::kTile == 16, "16x16 blocks");
     constexpr int kC = MM::kChunks;
-    __shared__ Acc red[3][kWave];
+    constexpr int kWaves = kDecodeThreads / kWave;
+    static_assert(kDepth >= 1 && kDepth * kC <= 4, "W tiles in flight per wave");
+    __shared__ Acc part[kDecodeMaxTiles][kWaves][kWave];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int frag_row = lane & 15, frag_grp = lane >> 4;
-    const int64_t kw0 = static_cast<int64_t>(wave) * kS * MM::kKStep;   // this wave's quarter of K
-    const int ntiles = static_cast<int>((N + 15) / 16);
-    const int G = static_cast<int>(gridDim.x);
+    const int64_t kw0 = static_cast<int64_t>(wave) * kS * MM::kKStep;   // this wave's eighth of K
+    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * cols;
+    const int64_t c1 = c0 + cols < N ? c0 + cols : N;                   // this block's columns [c0, c1)
+    const int nt = static_cast<int>((c1 - c0 + 15) / 16);              // 1 .. kDecodeMaxTiles
 
     v4i fx[kS][kC];
     {
@@ -697,10 +714,11 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_kernel(
             for (int c = 0; c < kC; ++c)
                 fx[s][c] = *reinterpret_cast<const v4i*>(xr + s * MM::kKStep + (frag_grp * kC + c) * 16);
     }
-    v4i fw[2][kS][kC];
+    v4i fw[kDepth][kS][kC];
     auto load_w = [&](v4i (&dst)[kS][kC], int t) {
-        int64_t n = static_cast<int64_t>(t) * 16 + frag_row;
-        n = n < N ? n : N - 1;
+        t = t < nt ? t : nt - 1;
+        int64_t n = c0 + static_cast<int64_t>(t) * 16 + frag_row;
+        n = n < c1 ? n : c1 - 1;
         const uint8_t* wr = wq + n * K + kw0;
 #pragma unroll
         for (int s = 0; s < kS; ++s)
@@ -708,41 +726,73 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_kernel(
             for (int c = 0; c < kC; ++c)
                 dst[s][c] = *reinterpret_cast<const v4i*>(wr + s * MM::kKStep + (frag_grp * kC + c) * 16);
     };
-    // Tile t with its W fragments in cur; the next tile's go into nxt first.
-    auto tile_step = [&](const v4i (&cur)[kS][kC], v4i (&nxt)[kS][kC], int t) {
-        if (t + G < ntiles) load_w(nxt, t + G);
-        Acc acc = MM::zero();
 #pragma unroll
-        for (int s = 0; s < kS; ++s) acc = MM::run(cur[s], fx[s], acc);
-        if (wave > 0) red[wave - 1][lane] = acc;
-        __syncthreads();
-        if (wave == 0) {
-            Acc a = acc;
+    for (int i = 0; i < kDepth; ++i) load_w(fw[i], i);
+    // Fully unrolled, so that the compiler counts the loads in flight exactly: across a loop's back
+    // edge, or after a branch that skips loads, it waits for more of them than needed.  The last
+    // group of kDepth tiles has a copy of its own without refills; in the other groups every
+    // buffer is refilled (with the last tile again when fewer tiles remain).
 #pragma unroll
-            for (int w = 0; w < 3; ++w) a += red[w][lane];
-            store_block<MM, kOutAcc>(a, 0, static_cast<int64_t>(t) * 16, lane, M, N, x_scale, w_scale,
-                                     tensor_scales != 0, y, out_acc);
+    for (int t0 = 0; t0 < kDecodeMaxTiles; t0 += kDepth) {
+        auto product = [&](int i) {
+            Acc acc = MM::zero();
+#pragma unroll
+            for (int s = 0; s < kS; ++s) acc = MM::run(fw[i][s], fx[s], acc);
+            // past the last tile a buffer holds the last tile again: the same sums, rewritten
+            part[t0 + i < nt ? t0 + i : nt - 1][wave][lane] = acc;
+        };
+        if (t0 + kDepth >= nt || t0 + kDepth >= kDecodeMaxTiles) {
+#pragma unroll
+            for (int i = 0; i < kDepth; ++i) product(i);
+            break;
         }
-        __syncthreads();                 // red is reused by the next tile
-    };
-    int t = blockIdx.x;
-    if (t < ntiles) load_w(fw[0], t);
-    for (; t < ntiles; t += 2 * G) {     // the register buffers alternate with compile-time indices
-        tile_step(fw[0], fw[1], t);
-        if (t + G < ntiles) tile_step(fw[1], fw[0], t + G);
+#pragma unroll
+        for (int i = 0; i < kDepth; ++i) {      // buffer i holds tile t0 + i
+            product(i);
+            load_w(fw[i], t0 + i + kDepth);
+            // keep the program order: the compiler would otherwise move the refills behind the
+            // later tiles' products
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    __syncthreads();
+    // The block's outputs: wave w adds the partials of tiles w, w + 8, ... and stores them.
+    for (int t = wave; t < nt; t += kWaves) {
+        Acc acc = part[t][0][lane];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) acc += part[t][w][lane];
+        store_block<MM, kOutAcc>(acc, 0, c0 + static_cast<int64_t>(t) * 16, lane, M, N, x_scale, w_scale,
+                                 tensor_scales != 0, y, out_acc, c1);
     }
 }
 
 template <typename M16, typename MT, bool kOutAcc>
 hipError_t gemm_dispatch(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale,
                          int64_t M, int64_t N, int64_t K, uint16_t* y, void* out_acc, int tensor, hipStream_t st) {
-    if (M <= 16 && K == 4 * 16 * M16::kKStep) {
-        // decode shape: X in registers, persistent grid with an equal number of tiles per block
-        const int64_t ntiles = (N + 15) / 16;
-        const int64_t per_block = (ntiles + 511) / 512;
-        const int64_t grid = (ntiles + per_block - 1) / per_block;
-        hipLaunchKernelGGL((gemm_decode_kernel<16, M16, kOutAcc>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
-                           st, xq, x_scale, wq, w_scale, M, N, K, y, out_acc, tensor);
+    if (M <= 16 && K == 8 * 8 * M16::kKStep) {
+        // decode shape: X in registers; each block an equal range of columns (a multiple of 8), one
+        // block per CU while that keeps a block's range within kDecodeMaxTiles tiles
+        const int64_t units = (N + 7) / 8;
+        int64_t per = (units + kDecodeBlocks - 1) / kDecodeBlocks;
+        if (per > 2 * kDecodeMaxTiles) per = 2 * kDecodeMaxTiles;
+        const int cols = static_cast<int>(per * 8);
+        const int64_t grid = (N + cols - 1) / cols;
+        const int tiles = (cols + 15) / 16;
+        const dim3 g(static_cast<unsigned>(grid)), b(kDecodeThreads);
+        if (tiles == 1) {
+            hipLaunchKernelGGL((gemm_decode_kernel<8, 1, M16, kOutAcc>), g, b, 0, st, xq, x_scale, wq, w_scale, M, N, K,
+                               y, out_acc, tensor, cols);
+        } else if (tiles == 2 || M16::kChunks > 1) {
+            hipLaunchKernelGGL((gemm_decode_kernel<8, 2, M16, kOutAcc>), g, b, 0, st, xq, x_scale, wq, w_scale, M, N, K,
+                               y, out_acc, tensor, cols);
+        } else if (tiles == 3) {
+            hipLaunchKernelGGL((gemm_decode_kernel<8, M16::kChunks == 1 ? 3 : 2, M16, kOutAcc>), g, b, 0, st, xq, x_scale,
+                               wq, w_scale, M, N, K, y, out_acc, tensor, cols);
+        } else {
+            hipLaunchKernelGGL((gemm_decode_kernel<8, M16::kChunks == 1 ? 4 : 2, M16, kOutAcc>), g, b, 0, st, xq, x_scale,
+                               wq, w_scale, M, N, K, y, out_acc, tensor, cols);
+        }
         return hipGetLastError();
     }
     if (M <= 16 || (M <= 32 && N <= 8192)) {

@@ -126,11 +126,16 @@ def check_sampled_rows(f, qtype, M, K, N):
         assert_rel_tol(yg, y64, 1e-2, extra=fp8_accumulation_bound(K, mag))
 
 
-@pytest.mark.parametrize("qtype,M,K,N", [("int8", 7, 4096, 9600), ("int8", 16, 4096, 1000), ("fp8", 5, 8192, 700)])
+@pytest.mark.parametrize("qtype,M,K,N", [("int8", 7, 4096, 9600), ("int8", 16, 4096, 1000), ("int8", 3, 4096, 8000),
+                                         ("int8", 2, 4096, 65560), ("fp8", 5, 8192, 700), ("fp8", 1, 8192, 2056),
+                                         ("fp8", 4, 8192, 8200)])
 def test_decode_shapes(f, qtype, M, K, N):
     """Decode-shaped GEMMs (M <= 16 with K = 4096 for INT8, 8192 for E4M3) take the kernel that keeps
-    X in registers and walks several output tiles per block: fewer rows than 16, a ragged last
-    tile, and blocks with one and with two tiles."""
+    X in registers and gives each block a contiguous range of columns (a multiple of 8), with as many
+    tiles in flight as the range has, up to 4 (INT8) or 2 (E4M3): fewer rows than 16; INT8 ranges of
+    40 columns (three tiles in flight, the last a half tile), 8, 32, and past 256 x 128 columns 128
+    (two groups of four, and a last range of 24); E4M3 ranges of 8 (a last one of 4), 16 and 40
+    (two groups of two, the second with a half tile and a repeat of it)."""
     announce(f"decode M={M} K={K} N={N} {qtype}")
     X = synth.random_matrix((M, K), seed=M + N, dtype="bf16", outliers=K // 100)
     W = synth.random_matrix((K, N), seed=K + N, dtype="bf16", scale=0.02)
