@@ -86,9 +86,10 @@ def test_big_tile_shapes(f, qtype, M, K, N):
 
 
 # (M, K, N) for each tile size below 256 x 256 (the largest with at least 192 tiles), all ragged:
-# 256 x 128 (217 tiles), 128 x 128 (192), 64 x 128 (192), and 64 x 64 with N too large for the
-# small-M kernel at M = 24.
-TILE_SHAPES = [(1700, 400, 3900), (1000, 528, 3000), (380, 272, 4090), (24, 1040, 9000)]
+# 256 x 128 (217 tiles; with K = 1552, 13 K steps: three rounds of the unrolled steady state, then
+# the guarded last steps with a partial K step), 128 x 128 (192), 64 x 128 (192), and 64 x 64 with
+# N too large for the small-M kernel at M = 24.
+TILE_SHAPES = [(1700, 400, 3900), (1800, 1552, 3900), (1000, 528, 3000), (380, 272, 4090), (24, 1040, 9000)]
 
 
 @pytest.mark.parametrize("M,K,N", TILE_SHAPES)
@@ -484,16 +485,26 @@ def division_rows(K, rows_per_col, seed):
     return X, s
 
 
-@pytest.mark.parametrize("qtype", ["int8", "fp8"])
-def test_division_through_row_scales(f, qtype):
+@pytest.mark.parametrize("qtype,launch_rows", [("int8", None), ("fp8", None), ("int8", 200), ("fp8", 200)])
+def test_division_through_row_scales(f, qtype, launch_rows):
     """X / s checked one quotient at a time: row m holds one nonzero X[m, m % K], divided by
     s[m % K], so x_scale[m] = |X / s| / Q exposes the rounding of that one division (subnormal
-    quotients included).  Codes and scales against the oracle's IEEE divisions, bit for bit."""
+    quotients included).  Codes and scales against the oracle's IEEE divisions, bit for bit.
+    launch_rows = 200: the rows go through in calls of 200 (and a last of 136), which take the
+    one-block-per-row kernel of small batches; None: one call, the many-rows kernel."""
     K, rows_per_col = 4096, 16
-    announce(f"division through row scales {qtype} M={K * rows_per_col} K={K}")
+    announce(f"division through row scales {qtype} M={K * rows_per_col} K={K} rows per call {launch_rows}")
     X, s = division_rows(K, rows_per_col, 91)
     assert np.isfinite(X).all()
-    xq, sx = f.w8a8_quant_act(dev(X), dev(s), qtype)
+    if launch_rows is None:
+        xq, sx = f.w8a8_quant_act(dev(X), dev(s), qtype)
+    else:
+        x, sd = dev(X), dev(s)
+        xq = torch.empty(X.shape, dtype=torch.uint8 if qtype == "fp8" else torch.int8, device="cuda")
+        sx = torch.empty(X.shape[0], dtype=torch.float32, device="cuda")
+        for r0 in range(0, X.shape[0], launch_rows):
+            r1 = min(r0 + launch_rows, X.shape[0])
+            f.w8a8_quant_act(x[r0:r1], sd, qtype, xq=xq[r0:r1], x_scale=sx[r0:r1])
     xq, sx = host(xq), host(sx)
     qx_ref, sx_ref = oracle.quant_act(X, s, qtype)
     np.testing.assert_array_equal(sx, sx_ref)
