@@ -87,15 +87,15 @@ __device__ __forceinline__ int out_col(int lane, int g) {
 
 // Dequantize and store four consecutive outputs of row m starting at column n (or store the raw
 // accumulators when kOutAcc).  tensor: one scale for all of W (w_scale[0]) instead of one per column.
-// Columns at or past ncap (<= N) are not stored.
+// Columns at or past ncap (<= N) are not stored; ld is the row stride of the output (>= N).
 template <bool kOutAcc, typename T>
 __device__ __forceinline__ void store4(const T (&a)[4], int64_t m, int64_t n, int64_t M, int64_t N, float sxm,
                                        const float* __restrict__ w_scale, bool tensor, uint16_t* __restrict__ y,
-                                       void* __restrict__ out_acc, int64_t ncap) {
+                                       void* __restrict__ out_acc, int64_t ncap, int64_t ld) {
     if (m >= M) return;
     if constexpr (kOutAcc) {
-        T* p = static_cast<T*>(out_acc) + m * N + n;
-        if (n + 3 < ncap && (N & 3) == 0) {
+        T* p = static_cast<T*>(out_acc) + m * ld + n;
+        if (n + 3 < ncap && (ld & 3) == 0) {
             typedef T v4t __attribute__((ext_vector_type(4)));
             *reinterpret_cast<v4t*>(p) = v4t{a[0], a[1], a[2], a[3]};
         } else {
@@ -111,8 +111,8 @@ __device__ __forceinline__ void store4(const T (&a)[4], int64_t m, int64_t n, in
             v[r] = (static_cast<float>(a[r]) * sxm) * swn;
         }
         const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
-        uint16_t* p = y + m * N + n;
-        if (n + 3 < ncap && (N & 3) == 0) {
+        uint16_t* p = y + m * ld + n;
+        if (n + 3 < ncap && (ld & 3) == 0) {
             *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
         } else {
             const uint16_t h[4] = {static_cast<uint16_t>(lo), static_cast<uint16_t>(lo >> 16),
@@ -130,14 +130,15 @@ template <typename MM, bool kOutAcc>
 __device__ __forceinline__ void store_block(const typename MM::Acc& acc, int64_t m_base, int64_t n_base, int lane,
                                             int64_t M, int64_t N, const float* __restrict__ x_scale,
                                             const float* __restrict__ w_scale, bool tensor,
-                                            uint16_t* __restrict__ y, void* __restrict__ out_acc, int64_t ncap) {
+                                            uint16_t* __restrict__ y, void* __restrict__ out_acc, int64_t ncap,
+                                            int64_t ld) {
     using T = typename std::remove_cv<typename std::remove_reference<decltype(acc[0])>::type>::type;
     const int64_t m = m_base + out_row<MM::kTile>(lane);
     const float sxm = (!kOutAcc && m < M) ? x_scale[tensor ? 0 : m] : 0.0f;
 #pragma unroll
     for (int g = 0; g < MM::kGroups; ++g) {
         const T a[4] = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
-        store4<kOutAcc>(a, m, n_base + out_col<MM::kTile>(lane, g), M, N, sxm, w_scale, tensor, y, out_acc, ncap);
+        store4<kOutAcc>(a, m, n_base + out_col<MM::kTile>(lane, g), M, N, sxm, w_scale, tensor, y, out_acc, ncap, ld);
     }
 }
 
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(kGM * kGN * kWave, 1)
 __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void gemm_tile_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ x_scale, const uint8_t* __restrict__ wq,
     const float* __restrict__ w_scale, int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y,
-    void* __restrict__ out_acc, int tiles_m, int tiles_n, int group_m, int tensor_scales) {
+    void* __restrict__ out_acc, int tiles_m, int tiles_n, int group_m, int tensor_scales, int64_t ldy) {
     using Acc = typename MM::Acc;
     constexpr int kWaves = kGM * kGN;                 // a kGM x kGN grid of waves
     constexpr int kWM = kBM / kGM, kWN = kBN / kGN;   // each wave's kWM x kWN outputs
@@ -534,7 +535,7 @@ __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void gemm_til
 #pragma unroll
             for (int j = 0; j < kNT; ++j)
                 store_block<MM, kOutAcc>(acc[i][j], mw0 + i * MM::kTile, nw0 + j * MM::kTile, lane, M, N, x_scale,
-                                         w_scale, tensor_scales != 0, y, out_acc, N);
+                                         w_scale, tensor_scales != 0, y, out_acc, N, ldy);
     } else {
         // Dequantize in registers, stage the wave's kWM x kWN bf16 tile in LDS (rows padded to
         // kOutStride bytes), and write it back as 16-byte pieces of whole output rows.
@@ -558,14 +559,14 @@ __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void gemm_til
                 }
         wait_lds_reads();                // this wave's LDS writes are complete before it reads them
         constexpr int kPieces = kWM * kWN * 2 / 16;  // 16-byte pieces in the wave's tile
-        const bool vec_ok = (N % 8) == 0;
+        const bool vec_ok = (ldy % 8) == 0;
 #pragma unroll
         for (int p = lane; p < kPieces; p += kWave) {
             const int row = p / (kWN / 8), c = p % (kWN / 8);
             const int64_t m = mw0 + row, n = nw0 + c * 8;
             const uint4 v = *reinterpret_cast<const uint4*>(ot + row * kOutStride + c * 16);
             if (m >= M) continue;
-            uint16_t* dst = y + m * N + n;
+            uint16_t* dst = y + m * ldy + n;
             if (vec_ok && n + 7 < N) {
                 *reinterpret_cast<uint4*>(dst) = v;
             } else {
@@ -660,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void gemm_small_m_kernel(
 #pragma unroll
             for (int w = 0; w < 3; ++w) a += red[w][i][lane];
             store_block<MM, kOutAcc>(a, static_cast<int64_t>(i) * 16, n0, lane, M, N, x_scale, w_scale,
-                                     tensor_scales != 0, y, out_acc, N);
+                                     tensor_scales != 0, y, out_acc, N, N);
         }
     }
 }
@@ -763,7 +764,7 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) acc += part[t][w][lane];
         store_block<MM, kOutAcc>(acc, 0, c0 + static_cast<int64_t>(t) * 16, lane, M, N, x_scale, w_scale,
-                                 tensor_scales != 0, y, out_acc, c1);
+                                 tensor_scales != 0, y, out_acc, c1, N);
     }
 }
 
@@ -813,24 +814,46 @@ hipError_t gemm_dispatch(const uint8_t* xq, const float* x_scale, const uint8_t*
     constexpr int64_t kFill = 192;
     const int group_m = 4;
     auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    auto launch = [&](auto kernel, int bm, int bn, int threads) {
+    // One launch over the output columns [n_off, n_off + ncols): the weight rows, column scales and
+    // outputs of that range, the output rows keeping their full stride N.
+    auto launch = [&](auto kernel, int bm, int bn, int threads, int64_t n_off, int64_t ncols) {
         const int tiles_m = static_cast<int>((M + bm - 1) / bm);
-        const int tiles_n = static_cast<int>((N + bn - 1) / bn);
-        hipLaunchKernelGGL(kernel, dim3(tiles_m * tiles_n), dim3(threads), 0, st, xq, x_scale, wq, w_scale, M, N, K, y,
-                           out_acc, tiles_m, tiles_n, group_m, tensor);
+        const int tiles_n = static_cast<int>((ncols + bn - 1) / bn);
+        const float* ws = (w_scale != nullptr && !tensor) ? w_scale + n_off : w_scale;
+        uint16_t* yo = y != nullptr ? y + n_off : nullptr;
+        void* acc = out_acc != nullptr ? static_cast<void*>(static_cast<uint8_t*>(out_acc) + n_off * 4) : nullptr;
+        hipLaunchKernelGGL(kernel, dim3(tiles_m * tiles_n), dim3(threads), 0, st, xq, x_scale, wq + n_off * K, ws, M,
+                           ncols, K, yo, acc, tiles_m, tiles_n, group_m, tensor, N);
     };
     if (tiles(256, 256) >= 512) {
         // Enough 256 x 256 tiles for two rounds over 256 CUs: 4 waves of 128 x 128 outputs, half the
         // LDS reads and two thirds of the copies per matrix-core instruction of the smaller tile.
-        launch(gemm_tile_kernel<256, 256, 2, 2, 2, 1, MT, kOutAcc>, 256, 256, 4 * kWave);
+        // A last round less than half full (MLP-up 8192 x 11008: 1376 tiles, 5.4 rounds) is moved to
+        // a second launch: the first n1 tile columns in whole rounds of 256 x 256 tiles, the rest of
+        // the columns in one round of 256 x 128 tiles (the last round then takes a 256 x 128 tile's
+        // time instead of a 256 x 256 tile's).
+        constexpr int64_t kCUs = 256;
+        const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256, rem = (tm * tn) % kCUs;
+        int64_t n1 = 0;
+        if (rem != 0 && rem < kCUs / 2) {
+            for (int64_t c = tn - 1; c >= 1 && n1 == 0; --c)
+                if ((tm * c) % kCUs == 0) n1 = c;
+            if (n1 > 0 && tm * ((N - 256 * n1 + 127) / 128) > kCUs) n1 = 0;
+        }
+        if (n1 > 0) {
+            launch(gemm_tile_kernel<256, 256, 2, 2, 2, 1, MT, kOutAcc>, 256, 256, 4 * kWave, 0, 256 * n1);
+            launch(gemm_tile_kernel<256, 128, 4, 2, 3, 2, MT, kOutAcc>, 256, 128, 8 * kWave, 256 * n1, N - 256 * n1);
+        } else {
+            launch(gemm_tile_kernel<256, 256, 2, 2, 2, 1, MT, kOutAcc>, 256, 256, 4 * kWave, 0, N);
+        }
     } else if (tiles(256, 128) >= kFill) {
-        launch(gemm_tile_kernel<256, 128, 4, 2, 3, 2, MT, kOutAcc>, 256, 128, 8 * kWave);
+        launch(gemm_tile_kernel<256, 128, 4, 2, 3, 2, MT, kOutAcc>, 256, 128, 8 * kWave, 0, N);
     } else if (tiles(128, 128) >= kFill) {
-        launch(gemm_tile_kernel<128, 128, 2, 2, 3, 1, MT, kOutAcc>, 128, 128, 4 * kWave);
+        launch(gemm_tile_kernel<128, 128, 2, 2, 3, 1, MT, kOutAcc>, 128, 128, 4 * kWave, 0, N);
     } else if (tiles(64, 128) >= kFill) {
-        launch(gemm_tile_kernel<64, 128, 1, 4, 3, 1, MT, kOutAcc>, 64, 128, 4 * kWave);
+        launch(gemm_tile_kernel<64, 128, 1, 4, 3, 1, MT, kOutAcc>, 64, 128, 4 * kWave, 0, N);
     } else {
-        launch(gemm_tile_kernel<64, 64, 2, 2, 3, 1, MT, kOutAcc>, 64, 64, 4 * kWave);
+        launch(gemm_tile_kernel<64, 64, 2, 2, 3, 1, MT, kOutAcc>, 64, 64, 4 * kWave, 0, N);
     }
     return hipGetLastError();
 }

@@ -77,11 +77,15 @@ def test_shapes_bf16(f, M, K, N, qtype):
     check_layer(run_layer(f, X, W, qtype=qtype), X, W, qtype=qtype)
 
 
-@pytest.mark.parametrize("qtype,M,K,N", [("int8", 5000, 1040, 6600), ("fp8", 4800, 1168, 6808)])
+@pytest.mark.parametrize("qtype,M,K,N", [("int8", 5000, 1040, 6600), ("fp8", 4800, 1168, 6808),
+                                         ("int8", 4000, 1040, 8300), ("fp8", 4000, 1040, 8300)])
 def test_big_tile_shapes(f, qtype, M, K, N):
     """Shapes with at least 512 tiles of 256 x 256 outputs take the two-stage 256 x 256 kernel: ragged
-    M, N and K (a partial last K step) with several steady-state K steps.  Codes and scales in full;
-    accumulators (INT8) and outputs on 64 sampled rows, including the first and the last."""
+    M, N and K (a partial last K step) with several steady-state K steps.  At 4000 x 8300 (16 x 33
+    tiles, a last round of 16) the columns split into two launches: 8192 columns of 256 x 256 tiles in
+    whole rounds, and the last 108 (a ragged 256 x 128 tile column) written at the full row stride.
+    Codes and scales in full; accumulators (INT8) and outputs on 64 sampled rows, including the first
+    and the last."""
     check_sampled_rows(f, qtype, M, K, N)
 
 
