@@ -1,10 +1,10 @@
 /*
  * libw8a8 - the W8A8 linear layer on AMD Instinct MI355X (gfx950).
  *
- * The layer Y = X W is computed as Y = (X diag(1/s)) (diag(s) W) with SmoothQuant factors s,
- * symmetric 8-bit quantization of both operands (one scale per token of X, one per output channel
- * of W), an 8-bit GEMM with 32-bit accumulation on the matrix cores, and a dequantizing epilogue
- * that writes bf16.  Sources, by page and section:
+ * The layer Y = X W is computed as Y = X~ W~ with X~[i, j] = X[i, j] / s_j and W~[j, n] = s_j W[j, n]
+ * (SmoothQuant factors s), symmetric 8-bit quantization of both operands (one scale per token of
+ * X, one per output channel of W), an 8-bit GEMM with 32-bit accumulation on the matrix cores,
+ * and a dequantizing epilogue that writes bf16.  Sources, by page and section:
  *   [WAQ] "Weight-Activation Quantization" (infra.bea.ai inference guide):
  *         s2 "The Problem: Activation Outliers"  symmetric INT8, scale = absmax / 127;
  *         s3 "SmoothQuant: The Smoothing Trick"  Y = XW = (X S^-1)(S W), divide activation

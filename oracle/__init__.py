@@ -158,7 +158,7 @@ def smooth_act(x, s=None):
 
 
 def smooth_weight(w, s=None):
-    """W~ = diag(s) W in float32."""
+    """W~[j, n] = s_j * W[j, n] in float32."""
     lib = _load()
     w, dt = _input(w)
     K, N = w.shape

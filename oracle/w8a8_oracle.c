@@ -119,7 +119,7 @@ void oracle_smooth_factors(const float* ax, const float* aw, int64_t K, double a
     for (int64_t j = 0; j < K; ++j) s[j] = oracle_smooth_factor(ax[j], aw[j], alpha);
 }
 
-/* X~ = X diag(s)^-1: each activation channel j divided by s_j ([WAQ] s3).  s == NULL means s = 1. */
+/* X~[i, j] = X[i, j] / s_j: each activation channel j divided by s_j ([WAQ] s3).  s == NULL means s = 1. */
 void oracle_smooth_act(const void* x, int dtype, int64_t M, int64_t K, const float* s, float* xs) {
     for (int64_t i = 0; i < M; ++i)
         for (int64_t j = 0; j < K; ++j) {
@@ -128,7 +128,7 @@ void oracle_smooth_act(const void* x, int dtype, int64_t M, int64_t K, const flo
         }
 }
 
-/* W~ = diag(s) W: each weight channel (row j of W [K, N]) multiplied by s_j ([WAQ] s3). */
+/* W~[j, n] = s_j W[j, n]: each weight channel (row j of W [K, N]) multiplied by s_j ([WAQ] s3). */
 void oracle_smooth_weight(const void* w, int dtype, int64_t K, int64_t N, const float* s, float* ws) {
     for (int64_t j = 0; j < K; ++j)
         for (int64_t n = 0; n < N; ++n) {
