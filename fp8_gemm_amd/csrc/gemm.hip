@@ -768,6 +768,115 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_kernel(
     }
 }
 
+// ------------------------------------------------------------------------------------------------
+// INT8 decode kernel with W staged through LDS (M <= 16, K = 4096).  The kernel above loads W
+// fragments straight into registers, and the matrix-core layout puts 16 different rows in 16
+// consecutive lanes, so each load instruction touches 16 rows x 64 bytes: read that way the
+// weights stream from HBM at about two thirds of what a contiguous read of the same bytes gets.
+// Here a block copies each 16-row tile of W (16 x 4096 bytes) into LDS with direct global -> LDS
+// copies of 1 KB of one row per wave instruction, and the waves read their fragments from LDS.
+// Within each 256-byte group of a row the 16-byte chunks are stored at chunk ^ (row % 16), which
+// the copies produce by permuting their source addresses inside the group, so that the 16 rows of
+// a fragment read fall in 16 different bank groups.  Two tile buffers (128 KB): the copies of tile
+// t + 1 are in flight while tile t is multiplied, and tile t + 2 is copied into t's buffer once
+// every wave has read it.  Column ranges, partial sums and stores are as in the kernel above (each
+// wave owns an eighth of K and keeps its X fragments for it in registers; the 8 partials are added
+// in LDS at the end).
+// ------------------------------------------------------------------------------------------------
+constexpr int kDecodeLdsK = 4096;
+
+template <bool kOutAcc>
+__global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ x_scale, const uint8_t* __restrict__ wq,
+    const float* __restrict__ w_scale, int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y,
+    void* __restrict__ out_acc, int tensor_scales, int cols) {
+    using MM = MmaI8x16;
+    using Acc = MM::Acc;
+    constexpr int kWaves = kDecodeThreads / kWave;
+    constexpr int kS = kDecodeLdsK / kWaves / MM::kKStep;             // 8 instructions per wave and tile
+    constexpr int kTileBytes = 16 * kDecodeLdsK;
+    constexpr int kCopies = kTileBytes / 1024 / kWaves;               // 8 copies per wave and tile
+    __shared__ __attribute__((aligned(1024))) uint8_t buf[2][kTileBytes];
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int lane = threadIdx.x % kWave;
+    const int frag_row = lane & 15, frag_grp = lane >> 4;
+    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * cols;
+    const int64_t c1 = c0 + cols < N ? c0 + cols : N;
+    const int nt = static_cast<int>((c1 - c0 + 15) / 16);              // 1 .. kDecodeMaxTiles
+
+    // Copy i of this wave of a 16-row tile whose row r starts at src + row_off(r): row
+    // r = (kCopies wave + i) / 4 of the tile, quarter q of the row; lane l fills stored chunk
+    // 64 q + l, which holds logical chunk (64 q + l) ^ r.
+    auto copy_rows = [&](const uint8_t* src, auto row_off, uint8_t* dst) {
+#pragma unroll
+        for (int i = 0; i < kCopies; ++i) {
+            const int inst = kCopies * wave + i;
+            const int r = inst >> 2, q = inst & 3;
+            const uint32_t off = row_off(r) + static_cast<uint32_t>(((64 * q + lane) ^ r) * 16);
+            copy_sv(src, off, lds_addr(dst) + static_cast<uint32_t>(r * kDecodeLdsK + q * 1024));
+        }
+    };
+    auto copy_tile = [&](int t, uint8_t* dst) {        // rows past c1 re-read row c1 - 1
+        copy_rows(wq, [&](int r) {
+            int64_t n = c0 + static_cast<int64_t>(t) * 16 + r;
+            n = n < c1 ? n : c1 - 1;
+            return static_cast<uint32_t>(n * K);
+        }, dst);
+    };
+    // Fragment of row frag_row, K step s of this wave's eighth, from a tile in LDS.
+    auto frag = [&](const uint8_t* b, int s) {
+        const int chunk = (wave * kS + s) * (MM::kKStep / 16) + frag_grp;
+        return *reinterpret_cast<const v4i*>(b + frag_row * kDecodeLdsK + ((chunk ^ frag_row) << 4));
+    };
+    // X goes through LDS too, next to tile 0: every global read of the kernel is then one of these
+    // copies, whose waits are explicit (a plain load would make the compiler's own wait for it
+    // count the copies issued after it, and wait for them as well).  X rows past M re-read row M - 1.
+    copy_rows(xq, [&](int r) { return static_cast<uint32_t>((r < M ? r : M - 1) * K); }, buf[1]);
+    copy_tile(0, buf[0]);
+    wait_copies<kCopies>();                           // X has landed; tile 0 may be in flight
+    block_barrier();
+    v4i fx[kS];
+#pragma unroll
+    for (int s = 0; s < kS; ++s) fx[s] = frag(buf[1], s);
+    wait_lds_reads();
+    block_barrier();                                  // every wave has read X: buffer 1 is free
+    if (nt > 1) copy_tile(1, buf[1]);
+    Acc acc[kDecodeMaxTiles];
+#pragma unroll
+    for (int t = 0; t < kDecodeMaxTiles; ++t) acc[t] = MM::zero();
+    // Fully unrolled (at most kDecodeMaxTiles tiles) so that acc[t] has compile-time indices.
+#pragma unroll
+    for (int t = 0; t < kDecodeMaxTiles; ++t) {
+        if (t >= nt) break;
+        if (t + 1 < nt) wait_copies<kCopies>();       // tile t landed; tile t + 1 may be in flight
+        else wait_copies<0>();
+        block_barrier();
+#pragma unroll
+        for (int s = 0; s < kS; ++s) {
+            const v4i w = frag(buf[t & 1], s);
+            acc[t] = MM::run(&w, &fx[s], acc[t]);
+        }
+        wait_lds_reads();
+        block_barrier();                              // every wave has read buffer t & 1
+        if (t + 2 < nt) copy_tile(t + 2, buf[t & 1]);
+    }
+    // The partial sums of the 8 waves meet in LDS (the tile buffers are free): wave w adds and
+    // stores tiles w, w + 8, ...
+    Acc* part = reinterpret_cast<Acc*>(&buf[0][0]);   // [tile][wave][lane]
+#pragma unroll
+    for (int t = 0; t < kDecodeMaxTiles; ++t)
+        if (t < nt) part[(t * kWaves + wave) * kWave + lane] = acc[t];
+    wait_lds_reads();
+    block_barrier();
+    for (int t = wave; t < nt; t += kWaves) {
+        Acc a = part[t * kWaves * kWave + lane];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) a += part[(t * kWaves + w) * kWave + lane];
+        store_block<MM, kOutAcc>(a, 0, c0 + static_cast<int64_t>(t) * 16, lane, M, N, x_scale, w_scale,
+                                 tensor_scales != 0, y, out_acc, c1, N);
+    }
+}
+
 template <typename M16, typename MT, bool kOutAcc>
 hipError_t gemm_dispatch(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale,
                          int64_t M, int64_t N, int64_t K, uint16_t* y, void* out_acc, int tensor, hipStream_t st) {
@@ -781,7 +890,10 @@ hipError_t gemm_dispatch(const uint8_t* xq, const float* x_scale, const uint8_t*
         const int64_t grid = (N + cols - 1) / cols;
         const int tiles = (cols + 15) / 16;
         const dim3 g(static_cast<unsigned>(grid)), b(kDecodeThreads);
-        if (tiles == 1) {
+        if (M16::kChunks == 1 && K == kDecodeLdsK && N * K < (int64_t(1) << 32)) {   // INT8: W through LDS
+            hipLaunchKernelGGL((gemm_decode_lds_kernel<kOutAcc>), g, b, 0, st, xq, x_scale, wq, w_scale, M, N, K, y,
+                               out_acc, tensor, cols);
+        } else if (tiles == 1) {
             hipLaunchKernelGGL((gemm_decode_kernel<8, 1, M16, kOutAcc>), g, b, 0, st, xq, x_scale, wq, w_scale, M, N, K,
                                y, out_acc, tensor, cols);
         } else if (tiles == 2 || M16::kChunks > 1) {
