@@ -60,13 +60,21 @@ __device__ __forceinline__ float smooth_chunks(float (&v)[kChunks][8], const flo
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[i][e] = div_by_rcp<kFp8>(v[i][e], sv[e], rv[e]);
                 } else {
+                    // The rare full-division path: one division at a time (interleaving 8 or 32 of
+                    // them would set the kernel's register count).
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) v[i][e] = div_rn(v[i][e], sv[e]);
+                    for (int e = 0; e < 8; ++e) {
+                        v[i][e] = div_rn(v[i][e], sv[e]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
         }
+        // Each chunk's s and 1 / s are read from LDS where they are used: hoisting the reads of all
+        // chunks would hold 16 registers per chunk at once.
+        if constexpr (kSmooth) __builtin_amdgcn_sched_barrier(0);
     }
     return amax;
 }
@@ -80,7 +88,14 @@ __device__ __forceinline__ void store_codes(const float (&v)[kChunks][8], float 
         if (c < nchunk) {
             float qv[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) qv[e] = kFast ? div_by_rcp<kFp8>(v[i][e], sc, rsc) : div_rn(v[i][e], sc);
+            for (int e = 0; e < 8; ++e) {
+                if constexpr (kFast) {
+                    qv[e] = div_by_rcp<kFp8>(v[i][e], sc, rsc);
+                } else {
+                    qv[e] = div_rn(v[i][e], sc);
+                    __builtin_amdgcn_sched_barrier(0);     // one full division at a time, as above
+                }
+            }
             const uint32_t lo = pack_codes4<kFp8>(qv[0], qv[1], qv[2], qv[3]);
             const uint32_t hi = pack_codes4<kFp8>(qv[4], qv[5], qv[6], qv[7]);
             *reinterpret_cast<uint2*>(qrow + c * 8) = make_uint2(lo, hi);
@@ -416,21 +431,13 @@ __device__ __forceinline__ void weight_tile_body(const void* __restrict__ w, int
     float* const row_s = L.row_s;
     const int64_t n0 = bx * kTN;
     const int64_t j0 = by * kTJ;
-    bool fast = true;
-    if (tid < kTN) {
-        const int64_t n = n0 + tid;
-        const float sc = (n < N) ? w_scale[n * scale_step] : 0.0f;
-        col_scale[tid] = sc;
-        col_rcp[tid] = div_rn(1.0f, sc);
-        fast = sc == 0.0f || in_pow2_range<-60, 60>(sc);
-    }
-    {
-        const int64_t j = j0 + tid;
-        row_s[tid] = (s && j < K) ? s[j] : 1.0f;
-    }
-    fast = __syncthreads_and(fast);
     const int wave = tid / kWave, lane = tid % kWave;
     const int cl = lane & 7, rl = lane >> 3;
+    // The column scale and s element of this thread, then the tile's loads, all issued before the
+    // staging and its barrier so that the tile is in flight meanwhile.
+    const int64_t n_t = n0 + tid, j_t = j0 + tid;
+    const float sc_t = (tid < kTN && n_t < N) ? w_scale[n_t * scale_step] : 0.0f;
+    const float s_t = (s && j_t < K) ? s[j_t] : 1.0f;
     // kTJ / 4 row groups x kTN / 8 column chunks, kItems (group, chunk) items per thread.  Item it of
     // wave w is combination b = kItems w + it: column chunk cc = cl + 8 (b / (kTJ / 32)), row group
     // g = rl + 8 (b % (kTJ / 32)).
@@ -441,6 +448,14 @@ __device__ __forceinline__ void weight_tile_body(const void* __restrict__ w, int
         const int cc = cl + 8 * (b / (kTJ / 32)), g = rl + 8 * (b % (kTJ / 32));
         load_item<kBf16, kVec>(w, K, N, j0 + 4 * g, n0 + 8 * cc, items[it]);
     }
+    bool fast = true;
+    if (tid < kTN) {
+        col_scale[tid] = sc_t;
+        col_rcp[tid] = div_rn(1.0f, sc_t);
+        fast = sc_t == 0.0f || in_pow2_range<-60, 60>(sc_t);
+    }
+    row_s[tid] = s_t;
+    fast = __syncthreads_and(fast);
 #pragma unroll
     for (int it = 0; it < kItems; ++it) {
         const int b = wave * kItems + it;
