@@ -334,10 +334,11 @@ hipError_t launch_absmax_rows(const void* a, bool bf16, int64_t R, int64_t C, fl
 hipError_t launch_absmax_tensor(const void* a, bool bf16, int64_t n, float divisor, float* out, hipStream_t st) {
     if (n <= 0) return hipSuccess;
     const int64_t nchunk = n / 8;
-    // At most 1024 blocks: every block ends with one atomic on the same address, and blocks that
-    // finish together queue behind each other there (4096 blocks over a freshly zeroed maximum
-    // doubled the time of a 134 MB pass).
-    const int64_t blocks = std::min<int64_t>((nchunk + 256 * 8 - 1) / (256 * 8), 1024);
+    // At most 256 blocks (one per CU): every block ends with one atomic on the same address, and
+    // blocks that finish together queue behind each other there.  Fill + maximum, graph replay over
+    // rotating buffers, at 1024 / 512 / 256 / 128 blocks: 33.5 MB 18.1 / 13.3 / 11.5 / 12.5 us,
+    // 470 MB 85.5 / 85.1 / 82.0 / 106.9 us.
+    const int64_t blocks = std::min<int64_t>((nchunk + 256 * 8 - 1) / (256 * 8), 256);
     if (bf16)
         hipLaunchKernelGGL(absmax_tensor_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a, nchunk,
                            divisor, out);
