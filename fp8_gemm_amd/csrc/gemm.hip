@@ -667,16 +667,16 @@ __global__ __launch_bounds__(kThreads) void gemm_small_m_kernel(
 }
 
 // ------------------------------------------------------------------------------------------------
-// Decode kernel (M <= 16, K = 8 * kS * kKStep): bound by reading W once.  A block has 8 waves; wave
-// w owns the w-th eighth of K and holds its X fragments for that eighth in registers for the whole
-// kernel, so X is read once per wave instead of once per output tile.  Block b owns the output
-// columns [b cols, (b + 1) cols): cols is a multiple of 8 chosen so that every CU streams the same
-// share of W (at N = 14336, 56 columns: three 16-column tiles and one of 8, whose other 8 rows
-// re-read the last row, from cache, and are not stored).  W fragments of kDepth tiles are in
-// flight per wave (at kDepth = 4 and 8 waves, 256 KB per block: the whole share at N = 14336), and
-// a buffer is refilled as soon as the matrix cores have consumed it.  kDepth is the block's tile
-// count, up to 4 (INT8) or 2 (E4M3, whose fragments are twice as large), so that no buffer is
-// loaded for a tile the block does not have.
+// Decode kernel (M <= 16, K = 8 * kS * kKStep; used for E4M3 at K = 8192, the INT8 decode shape
+// takes the LDS kernel below): bound by reading W once.  A block has 8 waves; wave w owns the w-th
+// eighth of K and holds its X fragments for that eighth in registers for the whole kernel, so X is
+// read once per wave instead of once per output tile.  Block b owns the output columns
+// [b cols, (b + 1) cols): cols is a multiple of 8 chosen so that every CU streams the same share of
+// W (at N = 14336, 56 columns: three 16-column tiles and one of 8, whose other 8 rows re-read the
+// last row, from cache, and are not stored).  W fragments of kDepth tiles are in flight per wave,
+// and a buffer is refilled as soon as the matrix cores have consumed it.  kDepth is the block's
+// tile count, up to 2 (E4M3 fragments are 32 bytes per lane), so that no buffer is loaded for a
+// tile the block does not have.
 // Each wave writes its partial sums per tile to LDS; after one barrier the partials are added
 // (exact for INT8) and stored, so no store sits between two waits for loads.
 // ------------------------------------------------------------------------------------------------
@@ -816,10 +816,13 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_kernel(
             copy_sv(src, off, lds_addr(dst) + static_cast<uint32_t>(r * kDecodeLdsK + q * 1024));
         }
     };
+    // W rows from the block's own first row, so that offsets stay within the block's columns
+    // (at most 2 kDecodeMaxTiles x 8 rows of 4 KB) for any N.
+    const uint8_t* const wblk = wq + c0 * K;
     auto copy_tile = [&](int t, uint8_t* dst) {        // rows past c1 re-read row c1 - 1
-        copy_rows(wq, [&](int r) {
-            int64_t n = c0 + static_cast<int64_t>(t) * 16 + r;
-            n = n < c1 ? n : c1 - 1;
+        copy_rows(wblk, [&](int r) {
+            int64_t n = static_cast<int64_t>(t) * 16 + r;
+            n = n < c1 - c0 ? n : c1 - c0 - 1;
             return static_cast<uint32_t>(n * K);
         }, dst);
     };
@@ -890,21 +893,16 @@ hipError_t gemm_dispatch(const uint8_t* xq, const float* x_scale, const uint8_t*
         const int64_t grid = (N + cols - 1) / cols;
         const int tiles = (cols + 15) / 16;
         const dim3 g(static_cast<unsigned>(grid)), b(kDecodeThreads);
-        if (M16::kChunks == 1 && K == kDecodeLdsK && N * K < (int64_t(1) << 32)) {   // INT8: W through LDS
+        if constexpr (M16::kChunks == 1) {              // INT8 (K = 4096): W through LDS
+            static_assert(8 * 8 * M16::kKStep == kDecodeLdsK, "the INT8 decode shape is K = 4096");
             hipLaunchKernelGGL((gemm_decode_lds_kernel<kOutAcc>), g, b, 0, st, xq, x_scale, wq, w_scale, M, N, K, y,
                                out_acc, tensor, cols);
-        } else if (tiles == 1) {
+        } else if (tiles == 1) {                        // E4M3 (K = 8192): fragments straight to registers
             hipLaunchKernelGGL((gemm_decode_kernel<8, 1, M16, kOutAcc>), g, b, 0, st, xq, x_scale, wq, w_scale, M, N, K,
                                y, out_acc, tensor, cols);
-        } else if (tiles == 2 || M16::kChunks > 1) {
+        } else {
             hipLaunchKernelGGL((gemm_decode_kernel<8, 2, M16, kOutAcc>), g, b, 0, st, xq, x_scale, wq, w_scale, M, N, K,
                                y, out_acc, tensor, cols);
-        } else if (tiles == 3) {
-            hipLaunchKernelGGL((gemm_decode_kernel<8, M16::kChunks == 1 ? 3 : 2, M16, kOutAcc>), g, b, 0, st, xq, x_scale,
-                               wq, w_scale, M, N, K, y, out_acc, tensor, cols);
-        } else {
-            hipLaunchKernelGGL((gemm_decode_kernel<8, M16::kChunks == 1 ? 4 : 2, M16, kOutAcc>), g, b, 0, st, xq, x_scale,
-                               wq, w_scale, M, N, K, y, out_acc, tensor, cols);
         }
         return hipGetLastError();
     }

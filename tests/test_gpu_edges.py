@@ -135,16 +135,52 @@ def check_sampled_rows(f, qtype, M, K, N):
                                          ("int8", 2, 4096, 65560), ("fp8", 5, 8192, 700), ("fp8", 1, 8192, 2056),
                                          ("fp8", 4, 8192, 8200)])
 def test_decode_shapes(f, qtype, M, K, N):
-    """Decode-shaped GEMMs (M <= 16 with K = 4096 for INT8, 8192 for E4M3) take the kernel that keeps
-    X in registers and gives each block a contiguous range of columns (a multiple of 8), with as many
-    tiles in flight as the range has, up to 4 (INT8) or 2 (E4M3): fewer rows than 16; INT8 ranges of
-    40 columns (three tiles in flight, the last a half tile), 8, 32, and past 256 x 128 columns 128
-    (two groups of four, and a last range of 24); E4M3 ranges of 8 (a last one of 4), 16 and 40
-    (two groups of two, the second with a half tile and a repeat of it)."""
+    """Decode-shaped GEMMs (M <= 16 with K = 4096 for INT8, 8192 for E4M3) give each block a
+    contiguous range of columns (a multiple of 8); INT8 stages the block's 16-row tiles through LDS,
+    E4M3 keeps up to 2 tiles of fragments in flight in registers: fewer rows than 16; INT8 ranges of
+    40 columns (three tiles, the last a half tile), 8, 32, and past 256 x 128 columns 128 (eight
+    tiles, and a last range of 24); E4M3 ranges of 8 (a last one of 4), 16 and 40 (two groups of
+    two, the second with a half tile and a repeat of it)."""
     announce(f"decode M={M} K={K} N={N} {qtype}")
     X = synth.random_matrix((M, K), seed=M + N, dtype="bf16", outliers=K // 100)
     W = synth.random_matrix((K, N), seed=K + N, dtype="bf16", scale=0.02)
     check_layer(run_layer(f, X, W, qtype=qtype), X, W, qtype=qtype)
+
+
+def _pattern_codes(n, k):
+    """INT8 weight codes in [-127, 127] that differ from row to row: ((31 n + 17 k + 5) mod 255) - 127."""
+    return (n * 31 + k * 17 + 5) % 255 - 127
+
+
+def test_decode_int8_weights_over_4gib(f):
+    """The INT8 decode kernel addresses W from each block's own first row, so a weight matrix of more
+    than 4 GiB (N K > 2^32 bytes) gives the oracle's accumulators and outputs on columns at the start,
+    on both sides of byte offset 2^32 and at the ragged end.  The weight codes follow a row-dependent
+    pattern, built on the device with torch and for the sampled rows on the host with numpy."""
+    M, K = 3, 4096
+    n_cross = (1 << 32) // K                      # the first row at byte offset 2^32
+    N = n_cross + 40
+    announce(f"decode int8 over 4 GiB M={M} K={K} N={N}")
+    wq = torch.empty((N, K), dtype=torch.int8, device="cuda")
+    kk = torch.arange(K, dtype=torch.int64, device="cuda")[None, :]
+    for n0 in range(0, N, 1 << 14):
+        n = torch.arange(n0, min(N, n0 + (1 << 14)), dtype=torch.int64, device="cuda")[:, None]
+        wq[n0:n0 + n.shape[0]] = _pattern_codes(n, kk).to(torch.int8)
+    rng = np.random.Generator(np.random.PCG64(4242))
+    qx = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    sx = rng.uniform(1e-3, 2e-3, M).astype(np.float32)
+    sw = rng.uniform(1e-3, 2e-3, N).astype(np.float32)
+    xq = dev(qx)
+    acc = f.w8a8_gemm_i32(xq, wq)
+    y = f.w8a8_gemm_dequant(xq, dev(sx), wq, dev(sw), "int8")
+    torch.cuda.synchronize()
+    cols = np.r_[0:16, n_cross - 24:n_cross + 24, N - 40:N]
+    qw = _pattern_codes(cols.astype(np.int64)[:, None], np.arange(K, dtype=np.int64)[None, :]).astype(np.int8)
+    a = oracle.gemm_i32(qx, qw)
+    np.testing.assert_array_equal(host(acc)[:, cols], a)
+    _, yb = oracle.dequant_i32(a, sx, sw[cols])
+    np.testing.assert_array_equal(host(y)[:, cols], yb)
+    del wq
 
 
 @pytest.mark.parametrize("M,K,N", [(3, 32, 5), (40, 512, 64), (129, 272, 203)])
