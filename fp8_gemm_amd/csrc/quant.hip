@@ -105,7 +105,7 @@ __device__ __forceinline__ void store_codes(const float (&v)[kChunks][8], float 
 
 // The body of a block (index bx) of kActWaves waves.  sh: kSmooth: s then 1/s, each K floats
 // (lds_half order); xchg: kSplit > 1: the parts' maxima of a row.
-template <bool kBf16, bool kFp8, int kChunks, bool kSmooth, int kSplit>
+template <bool kBf16, bool kFp8, int kChunks, bool kSmooth, int kSplit, bool kOneRow>
 __device__ __forceinline__ void quant_act_body(const void* __restrict__ x, const float* __restrict__ s, int64_t M,
                                                int64_t K, int rows_per_wave, uint8_t* __restrict__ q,
                                                float* __restrict__ scale, int64_t bx, float* sh,
@@ -114,17 +114,45 @@ __device__ __forceinline__ void quant_act_body(const void* __restrict__ x, const
     const int64_t nchunk = K / 8;
     float* const sh_s = sh;
     float* const sh_r = sh + K;
-    bool fast_s = true;
+    // A row is handled by kSplit consecutive waves, which take interleaved 512-element blocks of it.
+    constexpr int kRowsPerPass = kActWaves / kSplit;
+    const int slot = wave / kSplit;
+    const int part = wave % kSplit;
+    const int lane_c = part * kWave + lane;     // first chunk of this wave's share
+    constexpr int kStride = kSplit * kWave;
+    // Loads of the chunks of one row (all unconditional: chunks past the row end re-read the last
+    // chunk, which changes no maximum and is never stored), all issued before any conversion.
+    auto load_row = [&](Raw8<kBf16> (&raw)[kChunks], int64_t rrow) {
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) {
+            int64_t c = lane_c + static_cast<int64_t>(kStride) * i;
+            c = c < nchunk ? c : nchunk - 1;
+            raw[i] = load_raw8<kBf16>(x, rrow * K + c * 8);
+        }
+    };
+    // s is staged in LDS with its reciprocals.  kOneRow (rows_per_wave == 1, several waves per row;
+    // with one wave per row the compiler keeps the early row in scratch memory): the wave's one row is
+    // requested right after the s loads, so that it is in flight while the reciprocals are formed
+    // (the loads complete in order, so the wait for s does not wait for the row).
+    // K <= kSplit * kChunks * 512: at most kSplit * kChunks elements of s per thread, loaded
+    // together (indices past K re-read s[K - 1] and are not stored).
+    constexpr int kPer = kSmooth ? kSplit * kChunks : 1;
+    float sv[kPer];
     if constexpr (kSmooth) {
-        // K <= kSplit * kChunks * 512: at most kSplit * kChunks elements per thread, loaded
-        // together (indices past K re-read s[K - 1] and are not stored).
-        constexpr int kPer = kSplit * kChunks;
-        float sv[kPer];
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int64_t j = threadIdx.x + static_cast<int64_t>(i) * (kActWaves * kWave);
             sv[i] = s[j < K ? j : K - 1];
         }
+    }
+    Raw8<kBf16> first[kChunks];
+    if constexpr (kOneRow) {
+        const int64_t row = bx * kRowsPerPass + slot;
+        load_row(first, row < M ? row : M - 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    bool fast_s = true;
+    if constexpr (kSmooth) {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int64_t j = threadIdx.x + static_cast<int64_t>(i) * (kActWaves * kWave);
@@ -137,32 +165,24 @@ __device__ __forceinline__ void quant_act_body(const void* __restrict__ x, const
         }
         fast_s = __syncthreads_and(fast_s);
     }
-    // A row is handled by kSplit consecutive waves, which take interleaved 512-element blocks of it.
-    constexpr int kRowsPerPass = kActWaves / kSplit;
-    const int slot = wave / kSplit;
-    const int part = wave % kSplit;
-    const int lane_c = part * kWave + lane;     // first chunk of this wave's share
-    constexpr int kStride = kSplit * kWave;
     // One pass over the block's rows; X / s by div_by_rcp when fast.  Returns whether a row of this
     // wave came out with a scale outside [2^-60, 2^60] (or zero) after fast divisions: the guard
     // above does not hold there, so the block then takes a second pass with full divisions, in
     // which the same lanes rewrite the same codes and scales.
     auto rows_pass = [&](bool fast) {
         bool redo = false;
-        for (int rr = 0; rr < rows_per_wave; ++rr) {
-            const int64_t row = (bx * rows_per_wave + rr) * kRowsPerPass + slot;
+        const int nrows = kOneRow ? 1 : rows_per_wave;
+        for (int rr = 0; rr < nrows; ++rr) {
+            const int64_t row = (bx * nrows + rr) * kRowsPerPass + slot;
             const bool live = row < M;
             if (kSplit == 1 && !live) break;
             const int64_t rrow = live ? row : M - 1;
-            // All loads unconditional (chunks past the row end re-read the last chunk, which changes
-            // no maximum and is never stored) and issued before any conversion, so that they are all
-            // in flight at once.
             Raw8<kBf16> raw[kChunks];
+            if (kOneRow && fast) {
 #pragma unroll
-            for (int i = 0; i < kChunks; ++i) {
-                int64_t c = lane_c + static_cast<int64_t>(kStride) * i;
-                c = c < nchunk ? c : nchunk - 1;
-                raw[i] = load_raw8<kBf16>(x, rrow * K + c * 8);
+                for (int i = 0; i < kChunks; ++i) raw[i] = first[i];
+            } else {
+                load_row(raw, rrow);
             }
             float v[kChunks][8];
 #pragma unroll
@@ -205,13 +225,14 @@ __device__ __forceinline__ void quant_act_body(const void* __restrict__ x, const
     }
 }
 
-template <bool kBf16, bool kFp8, int kChunks, bool kSmooth, int kSplit>
+template <bool kBf16, bool kFp8, int kChunks, bool kSmooth, int kSplit, bool kOneRow>
 __global__ __launch_bounds__(kActWaves * kWave) void quant_act_kernel(
     const void* __restrict__ x, const float* __restrict__ s, int64_t M, int64_t K, int rows_per_wave,
     uint8_t* __restrict__ q, float* __restrict__ scale) {
     extern __shared__ float sh[];
     __shared__ float xchg[2][kActWaves];
-    quant_act_body<kBf16, kFp8, kChunks, kSmooth, kSplit>(x, s, M, K, rows_per_wave, q, scale, blockIdx.x, sh, xchg);
+    quant_act_body<kBf16, kFp8, kChunks, kSmooth, kSplit, kOneRow>(x, s, M, K, rows_per_wave, q, scale, blockIdx.x,
+                                                                   sh, xchg);
 }
 
 // Few rows: one block per row, so that the grid is as wide as the batch, and one round trip to
@@ -489,7 +510,7 @@ __global__ __launch_bounds__(256) void quant_weight_t_kernel(const void* __restr
 // Both need only s and the final weight scales, so blocks [0, nq) quantize activations (as
 // quant_act_kernel) and the others code two weight tiles each (as quant_weight_t_kernel, waves 0-3
 // and 4-7); tile 2b + 1 past the last tile is inactive.  One dynamic LDS buffer serves either role.
-template <bool kBf16, bool kFp8, int kChunks, int kSplit>
+template <bool kBf16, bool kFp8, int kChunks, int kSplit, bool kOneRow>
 __global__ __launch_bounds__(kActWaves * kWave) void quant_pair_kernel(
     const void* __restrict__ x, const float* __restrict__ s, int64_t M, int64_t K, int rows_per_wave,
     uint8_t* __restrict__ xq, float* __restrict__ x_scale, const void* __restrict__ w, int64_t N,
@@ -498,8 +519,8 @@ __global__ __launch_bounds__(kActWaves * kWave) void quant_pair_kernel(
     if (blockIdx.x < nq) {
         float* const sh = reinterpret_cast<float*>(lds4);
         float (*xchg)[kActWaves] = reinterpret_cast<float (*)[kActWaves]>(sh + 2 * K);
-        quant_act_body<kBf16, kFp8, kChunks, true, kSplit>(x, s, M, K, rows_per_wave, xq, x_scale, blockIdx.x, sh,
-                                                           xchg);
+        quant_act_body<kBf16, kFp8, kChunks, true, kSplit, kOneRow>(x, s, M, K, rows_per_wave, xq, x_scale,
+                                                                    blockIdx.x, sh, xchg);
     } else {
         const int half = threadIdx.x / 256;
         WeightTileLds* const L = reinterpret_cast<WeightTileLds*>(lds4) + half;
@@ -873,11 +894,15 @@ void quant_act_launch(const void* x, int64_t M, int64_t K, const float* s, uint8
     dim3 grid(static_cast<unsigned>((M + rows_per_block - 1) / rows_per_block)), block(kActWaves * kWave);
     if (s) {
         const size_t lds = 2 * static_cast<size_t>(K) * sizeof(float);
-        hipLaunchKernelGGL((quant_act_kernel<kBf16, kFp8, kChunks, true, kSplit>), grid, block, lds, st, x, s, M, K,
-                           rpw, xq, xs);
+        if (rpw == 1 && kSplit > 1)
+            hipLaunchKernelGGL((quant_act_kernel<kBf16, kFp8, kChunks, true, kSplit, kSplit != 1>), grid, block, lds, st, x, s,
+                               M, K, rpw, xq, xs);
+        else
+            hipLaunchKernelGGL((quant_act_kernel<kBf16, kFp8, kChunks, true, kSplit, false>), grid, block, lds, st, x, s,
+                               M, K, rpw, xq, xs);
     } else {
-        hipLaunchKernelGGL((quant_act_kernel<kBf16, kFp8, kChunks, false, kSplit>), grid, block, 0, st, x, s, M, K,
-                           rpw, xq, xs);
+        hipLaunchKernelGGL((quant_act_kernel<kBf16, kFp8, kChunks, false, kSplit, false>), grid, block, 0, st, x, s, M,
+                           K, rpw, xq, xs);
     }
 }
 
@@ -930,9 +955,15 @@ void quant_pair_launch(const void* x, int64_t M, int64_t K, const float* s, uint
     const int64_t ntiles = wtx * ((K + kTJ - 1) / kTJ);
     const size_t lds = std::max(2 * static_cast<size_t>(K) * sizeof(float) + 2 * kActWaves * sizeof(float),
                                 2 * sizeof(WeightTileLds));
-    hipLaunchKernelGGL((quant_pair_kernel<kBf16, kFp8, kChunks, kSplit>), dim3(static_cast<unsigned>(nq + (ntiles + 1) / 2)),
-                       dim3(kActWaves * kWave), lds, st, x, s, M, K, rpw, xq, xs, w, N, w_scale, wq,
-                       static_cast<unsigned>(nq), static_cast<unsigned>(wtx), static_cast<unsigned>(ntiles));
+    const dim3 grid(static_cast<unsigned>(nq + (ntiles + 1) / 2)), block(kActWaves * kWave);
+    if (rpw == 1 && kSplit > 1)
+        hipLaunchKernelGGL((quant_pair_kernel<kBf16, kFp8, kChunks, kSplit, kSplit != 1>), grid, block, lds, st, x, s, M, K,
+                           rpw, xq, xs, w, N, w_scale, wq, static_cast<unsigned>(nq), static_cast<unsigned>(wtx),
+                           static_cast<unsigned>(ntiles));
+    else
+        hipLaunchKernelGGL((quant_pair_kernel<kBf16, kFp8, kChunks, kSplit, false>), grid, block, lds, st, x, s, M, K,
+                           rpw, xq, xs, w, N, w_scale, wq, static_cast<unsigned>(nq), static_cast<unsigned>(wtx),
+                           static_cast<unsigned>(ntiles));
 }
 
 // K <= 8192, N % 8 == 0, M, N >= 1.

@@ -525,13 +525,15 @@ def division_rows(K, rows_per_col, seed):
     return X, s
 
 
-@pytest.mark.parametrize("qtype,launch_rows", [("int8", None), ("fp8", None), ("int8", 200), ("fp8", 200)])
+@pytest.mark.parametrize("qtype,launch_rows", [("int8", None), ("fp8", None), ("int8", 200), ("fp8", 200),
+                                               ("int8", 2048), ("fp8", 2048)])
 def test_division_through_row_scales(f, qtype, launch_rows):
     """X / s checked one quotient at a time: row m holds one nonzero X[m, m % K], divided by
     s[m % K], so x_scale[m] = |X / s| / Q exposes the rounding of that one division (subnormal
     quotients included).  Codes and scales against the oracle's IEEE divisions, bit for bit.
     launch_rows = 200: the rows go through in calls of 200 (and a last of 136), which take the
-    one-block-per-row kernel of small batches; None: one call, the many-rows kernel."""
+    one-block-per-row kernel of small batches; 2048: calls of 2048 rows, the many-rows kernel with one
+    row per wave pair (the row requested before s is staged); None: one call, the many-rows kernel."""
     K, rows_per_col = 4096, 16
     announce(f"division through row scales {qtype} M={K * rows_per_col} K={K} rows per call {launch_rows}")
     X, s = division_rows(K, rows_per_col, 91)
