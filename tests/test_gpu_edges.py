@@ -377,6 +377,45 @@ def test_e4m3_conversion_sweep(f):
         np.testing.assert_array_equal(xq, ref)
 
 
+@pytest.mark.parametrize("qtype", ["fp8", "int8"])
+def test_code_conversion_exhaustive(f, qtype):
+    """Every fp32 bit pattern in [-448, 448] (2 x 1,138,753,537 patterns, both zeros and all
+    subnormals included) through the per-tensor quantize with amax = Q (448 or 127), whose one
+    scale is exactly 1, so each code is the rounding of the value itself: E4M3 to nearest, ties to
+    even ("Weight-Activation Quantization", section 4: E4M3 codes of x / s over [-448, 448]), or
+    INT8 half to even and saturated at +-127 (section 2).  Against the oracle's conversion, in
+    chunks of 2^27 patterns; the oracle runs on 8 host threads per chunk."""
+    from concurrent.futures import ThreadPoolExecutor
+    top, chunk, K = 0x43E00000, 1 << 27, 4096
+    qmax = np.float32(448.0 if qtype == "fp8" else 127.0)
+    amax = torch.tensor([qmax], dtype=torch.float32, device="cuda")
+
+    def ref_of(part):
+        return oracle.quant_tensor(part, qmax, qtype)[0]
+
+    checked = 0
+    with ThreadPoolExecutor(8) as pool:
+        for sign in (0, 0x80000000):
+            for lo in range(0, top + 1, chunk):
+                hi = min(lo + chunk, top + 1)
+                announce(f"{qtype} exhaustive: sign {sign >> 31}, patterns {lo:#010x} .. {hi - 1:#010x}")
+                vals = (np.arange(lo, hi, dtype=np.uint32) | np.uint32(sign)).view(np.float32)
+                n = len(vals)
+                rows = (n + K - 1) // K
+                X = np.zeros(rows * K, np.float32)
+                X[:n] = vals
+                xq, sx, _ = f.w8a8_quant_act_tensor(dev(X.reshape(rows, K)), amax, qtype)
+                got = host(xq).reshape(-1)[:n].view(np.uint8)
+                assert host(sx)[0] == np.float32(1.0)
+                ref = np.concatenate(list(pool.map(ref_of, np.array_split(vals, 8)))).view(np.uint8)
+                bad = np.flatnonzero(got != ref)
+                assert bad.size == 0, (f"{bad.size} codes differ, first at value {vals[bad[0]]!r} "
+                                       f"(pattern {vals[bad[0]:bad[0] + 1].view(np.uint32)[0]:#010x}): "
+                                       f"GPU {got[bad[0]]:#04x}, oracle {ref[bad[0]]:#04x}")
+                checked += n
+    assert checked == 2 * (top + 1)
+
+
 def test_int8_extremes_and_determinism(f):
     """Codes of +-127 over long K reach the largest accumulators; two runs are bit-identical."""
     announce("int8 extremes")
