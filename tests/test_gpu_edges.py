@@ -65,6 +65,7 @@ SHAPES = [
     (1, 16, 1), (5, 48, 7), (16, 512, 512), (17, 256, 33), (33, 1024, 130), (64, 2048, 96),
     (65, 128, 128), (300, 592, 200), (257, 4096, 129), (512, 1040, 384),
     (70, 6160, 96),     # activation rows of 4097..8192 elements: four waves per row, ragged chunks
+    (1030, 4096, 64), (1027, 6160, 48),   # many-row quantize, one row per wave group, ragged last block
 ]
 
 
