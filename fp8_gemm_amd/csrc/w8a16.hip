@@ -252,9 +252,13 @@ __global__ __launch_bounds__(kThreads16) void w8a16_kernel(const uint16_t* __res
 }
 
 // ------------------------------------------------------------------------------------------------
-// Tiled kernel (batches past the decode shape): a block owns a kBM x kBN output tile; its 4 waves in
-// a 2 x 2 grid own (kBM / 2) x (kBN / 2) each, as 32 x 32 blocks of v_mfma_f32_32x32x16_bf16 (A = 32
-// output channels of W, B = 32 rows of X; lane l supplies row l % 32 and 8 k of each operand).
+// Tiled kernel (batches past the decode shape): a block owns a kBM x kBN output tile; its waves in a
+// kGM x kGN grid own (kBM / kGM) x (kBN / kGN) each, as 32 x 32 blocks of v_mfma_f32_32x32x16_bf16
+// (A = 32 output channels of W, B = 32 rows of X; lane l supplies row l % 32 and 8 k of each operand).
+// 128 x 128 tiles take 4 waves of 64 x 64 (two blocks per CU); 256 x 256 tiles take 8 waves of
+// 128 x 64 (one block per CU, two waves per SIMD), which moves a third less through LDS per product:
+// per K step and CU, 128 KB of fragment reads and staging against 96 KB for two 128 x 128 blocks
+// with the same matrix-core work halved.
 // K is taken 32 at a time.  Both operands go through LDS as bf16: the W codes are converted once,
 // while staged, so each W element is converted once per block and both tiles share one layout:
 // 64 bytes per row and K step, as four 16-byte chunks; chunk c of row r is stored at chunk
@@ -265,19 +269,20 @@ __global__ __launch_bounds__(kThreads16) void w8a16_kernel(const uint16_t* __res
 // N re-read the last row (never stored); the k past K (K % 32 = 16) are zero.
 // ------------------------------------------------------------------------------------------------
 typedef float v16f __attribute__((ext_vector_type(16)));
+constexpr int kW8a16Big = 192;           // 256 x 256 tiles from this many on (three quarters of the CUs)
 constexpr int kKS = 32;                  // k per step
 constexpr int kRowBytes = kKS * 2;       // bytes per row and step (bf16)
 
 __device__ __forceinline__ int tswz(int row, int chunk) { return row * kRowBytes + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
-template <int kBM, int kBN>
-__global__ __launch_bounds__(256, 2) void w8a16_tile_kernel(const uint16_t* __restrict__ x, const int8_t* __restrict__ wq,
-                                                            const float* __restrict__ w_scale, int64_t M, int64_t N,
-                                                            int64_t K, uint16_t* __restrict__ y, int tiles_m,
-                                                            int tiles_n) {
-    constexpr int kMT = kBM / 64, kNT = kBN / 64;           // 32 x 32 blocks per wave along M and N
+template <int kBM, int kBN, int kGM, int kGN, int kBlocksPerCU>
+__global__ __launch_bounds__(kGM * kGN * kWave, kBlocksPerCU) void w8a16_tile_kernel(
+    const uint16_t* __restrict__ x, const int8_t* __restrict__ wq, const float* __restrict__ w_scale, int64_t M,
+    int64_t N, int64_t K, uint16_t* __restrict__ y, int tiles_m, int tiles_n) {
+    constexpr int kWM = kBM / kGM, kWN = kBN / kGN;         // each wave's outputs
+    constexpr int kMT = kWM / 32, kNT = kWN / 32;           // 32 x 32 blocks per wave along M and N
     constexpr int kXChunks = kBM * 4, kWChunks = kBN * 2;  // 16-byte X chunks, 16-code W chunks per step
-    constexpr int kThreads = 256;
+    constexpr int kThreads = kGM * kGN * kWave;
     constexpr int kXPer = (kXChunks + kThreads - 1) / kThreads, kWPer = (kWChunks + kThreads - 1) / kThreads;
     constexpr int kXStage = kBM * kRowBytes, kWStage = kBN * kRowBytes;
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (kXStage + kWStage)];
@@ -296,11 +301,11 @@ __global__ __launch_bounds__(256, 2) void w8a16_tile_kernel(const uint16_t* __re
     const int64_t m0 = static_cast<int64_t>(first + in % gm) * kBM, n0 = static_cast<int64_t>(in / gm) * kBN;
 
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int wm = wave / 2, wn = wave % 2;
+    const int wm = wave / kGN, wn = wave % kGN;
     const int r32 = lane % 32, g32 = lane / 32;
 
-    // Staging: X chunk p = tid + 256 i is row p / 4, chunk p % 4 (8 bf16); W chunk p = tid + 256 i
-    // is row p / 2, half p % 2 (16 codes, two bf16 chunks).
+    // Staging: X chunk p = tid + kThreads i is row p / 4, chunk p % 4 (8 bf16); W chunk p = tid +
+    // kThreads i is row p / 2, half p % 2 (16 codes, two bf16 chunks).
     const uint16_t* xsrc[kXPer];
     int xl[kXPer], xk[kXPer];
 #pragma unroll
@@ -369,10 +374,10 @@ __global__ __launch_bounds__(256, 2) void w8a16_tile_kernel(const uint16_t* __re
             v8bf fx[kMT], fw[kNT];
 #pragma unroll
             for (int i = 0; i < kMT; ++i)
-                fx[i] = *reinterpret_cast<const v8bf*>(xs + stage * kXStage + tswz(wm * (kBM / 2) + 32 * i + r32, 2 * u + g32));
+                fx[i] = *reinterpret_cast<const v8bf*>(xs + stage * kXStage + tswz(wm * kWM + 32 * i + r32, 2 * u + g32));
 #pragma unroll
             for (int j = 0; j < kNT; ++j)
-                fw[j] = *reinterpret_cast<const v8bf*>(ws + stage * kWStage + tswz(wn * (kBN / 2) + 32 * j + r32, 2 * u + g32));
+                fw[j] = *reinterpret_cast<const v8bf*>(ws + stage * kWStage + tswz(wn * kWN + 32 * j + r32, 2 * u + g32));
 #pragma unroll
             for (int i = 0; i < kMT; ++i)
 #pragma unroll
@@ -388,17 +393,17 @@ __global__ __launch_bounds__(256, 2) void w8a16_tile_kernel(const uint16_t* __re
         step(t + 1, std::integral_constant<int, 1>{});
     }
     if (t < nk) step(t, std::integral_constant<int, 0>{});
-    // Lane results of block (i, j): row m = m0 + wm (kBM / 2) + 32 i + r32, columns
-    // n = n0 + wn (kBN / 2) + 32 j + 8 q + 4 g32 + r (r = 0..3) in acc[4 q + r].
+    // Lane results of block (i, j): row m = m0 + wm kWM + 32 i + r32, columns
+    // n = n0 + wn kWN + 32 j + 8 q + 4 g32 + r (r = 0..3) in acc[4 q + r].
 #pragma unroll
     for (int j = 0; j < kNT; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int64_t n = n0 + wn * (kBN / 2) + 32 * j + 8 * q + 4 * g32;
+            const int64_t n = n0 + wn * kWN + 32 * j + 8 * q + 4 * g32;
             const v4f sc = load_scales4(w_scale, n, N);
 #pragma unroll
             for (int i = 0; i < kMT; ++i) {
-                const int64_t m = m0 + wm * (kBM / 2) + 32 * i + r32;
+                const int64_t m = m0 + wm * kWM + 32 * i + r32;
                 const v4f a = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
                 store_w8a16(a, sc, m, n, M, N, y);
             }
@@ -431,14 +436,19 @@ hipError_t launch_gemm_w8a16(const uint16_t* x, const int8_t* wq, const float* w
                            dim3(kThreads16), 0, st, x, wq, w_scale, M, N, K, y);
         return hipGetLastError();
     }
-    // Tiled: 128 x 128 tiles when there are enough of them for two per CU, else 64 x 64.
-    auto launch_tiled = [&](auto kernel, int bm, int bn) {
+    // Tiled: 256 x 256 tiles when there are enough of them for about one per CU, else 128 x 128 when
+    // there are enough for one and a half per CU, else 64 x 64.
+    auto launch_tiled = [&](auto kernel, int bm, int bn, int threads) {
         const int tm = static_cast<int>((M + bm - 1) / bm), tn = static_cast<int>((N + bn - 1) / bn);
-        hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(tm * tn)), dim3(256), 0, st, x, wq, w_scale, M, N, K, y,
-                           tm, tn);
+        hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(tm * tn)), dim3(threads), 0, st, x, wq, w_scale, M, N, K,
+                           y, tm, tn);
     };
-    if (((M + 127) / 128) * ((N + 127) / 128) >= 512) launch_tiled(w8a16_tile_kernel<128, 128>, 128, 128);
-    else launch_tiled(w8a16_tile_kernel<64, 64>, 64, 64);
+    if (((M + 255) / 256) * ((N + 255) / 256) >= kW8a16Big)
+        launch_tiled(w8a16_tile_kernel<256, 256, 2, 4, 1>, 256, 256, 512);
+    else if (((M + 127) / 128) * ((N + 127) / 128) >= 384)
+        launch_tiled(w8a16_tile_kernel<128, 128, 2, 2, 2>, 128, 128, 256);
+    else
+        launch_tiled(w8a16_tile_kernel<64, 64, 2, 2, 2>, 64, 64, 256);
     return hipGetLastError();
 }
 

@@ -9,8 +9,9 @@ Bar:
     accumulation error of the matrix cores (gpu_util.fp8_accumulation_bound, which also covers an
     fp32 accumulation of exact products).
 Shapes cover the decode kernel (M <= 16, K = 4096), the small-M kernel (up to 128 rows on narrow
-layers), and the tiled kernel with 64 x 64 and 128 x 128 tiles (ragged M and N, fewer rows than
-one tile, a K that ends in half a 32-wide step, a grid that does not divide into the 8 XCDs).
+layers), and the tiled kernel with 64 x 64, 128 x 128 and 256 x 256 tiles (ragged M and N, fewer
+rows than one tile, a K that ends in half a 32-wide step, a grid that does not divide into the 8
+XCDs).
 """
 import numpy as np
 import pytest
@@ -35,7 +36,8 @@ def f():
 # (M, K, N): decode kernel; general kernel with one row block, with four, several row blocks
 SHAPES = [(1, 4096, 1000), (7, 4096, 4100), (16, 4096, 96), (5, 528, 77), (40, 1040, 300), (300, 4096, 130),
           (129, 2064, 517), (17, 48, 33), (100, 528, 8200), (1000, 1040, 1000), (2050, 272, 4100),
-          (4096, 4096, 4096)]
+          (4096, 4096, 4096),
+          (3000, 1040, 4200), (2600, 272, 5100)]   # 256 x 256 tiles: ragged M, N and K, 220 blocks
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
