@@ -894,9 +894,10 @@ void quant_act_launch(const void* x, int64_t M, int64_t K, const float* s, uint8
     dim3 grid(static_cast<unsigned>((M + rows_per_block - 1) / rows_per_block)), block(kActWaves * kWave);
     if (s) {
         const size_t lds = 2 * static_cast<size_t>(K) * sizeof(float);
+        // One row per wave group: the early-row form (instantiated for kSplit > 1 only).
         if (rpw == 1 && kSplit > 1)
-            hipLaunchKernelGGL((quant_act_kernel<kBf16, kFp8, kChunks, true, kSplit, kSplit != 1>), grid, block, lds, st, x, s,
-                               M, K, rpw, xq, xs);
+            hipLaunchKernelGGL((quant_act_kernel<kBf16, kFp8, kChunks, true, kSplit, kSplit != 1>), grid, block, lds,
+                               st, x, s, M, K, rpw, xq, xs);
         else
             hipLaunchKernelGGL((quant_act_kernel<kBf16, kFp8, kChunks, true, kSplit, false>), grid, block, lds, st, x, s,
                                M, K, rpw, xq, xs);
@@ -956,7 +957,7 @@ void quant_pair_launch(const void* x, int64_t M, int64_t K, const float* s, uint
     const size_t lds = std::max(2 * static_cast<size_t>(K) * sizeof(float) + 2 * kActWaves * sizeof(float),
                                 2 * sizeof(WeightTileLds));
     const dim3 grid(static_cast<unsigned>(nq + (ntiles + 1) / 2)), block(kActWaves * kWave);
-    if (rpw == 1 && kSplit > 1)
+    if (rpw == 1 && kSplit > 1)          // the early-row form, as in quant_act_launch
         hipLaunchKernelGGL((quant_pair_kernel<kBf16, kFp8, kChunks, kSplit, kSplit != 1>), grid, block, lds, st, x, s, M, K,
                            rpw, xq, xs, w, N, w_scale, wq, static_cast<unsigned>(nq), static_cast<unsigned>(wtx),
                            static_cast<unsigned>(ntiles));
