@@ -139,10 +139,11 @@ def test_smooth_quant_empty(f, M, N):
         np.testing.assert_array_equal(codes(host(r["xq"])), codes(qx))
 
 
-@pytest.mark.parametrize("name", ["c3", "c5"])
+@pytest.mark.parametrize("name", ["c1", "c3", "c4", "c5"])
 def test_smooth_quant_large_workloads(f, name):
-    """The MLP-up (INT8) and large FP8 workloads at full size, as the benchmark step runs them:
-    maxima, s, weight codes and scales, activation codes and scales bit-exact."""
+    """The tiny, MLP-up (INT8), decode and large FP8 workloads at full size (the prefill one has
+    its own test), as the benchmark step runs them: maxima, s, weight codes and scales, activation
+    codes and scales bit-exact."""
     wl = synth.workload(name)
     announce(f"smooth_quant {wl.name}")
     X, W = synth.make_inputs(wl, seed=0)
