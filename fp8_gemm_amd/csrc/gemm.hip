@@ -568,7 +568,10 @@ __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void gemm_til
             if (m >= M) continue;
             uint16_t* dst = y + m * ldy + n;
             if (vec_ok && n + 7 < N) {
-                *reinterpret_cast<uint4*>(dst) = v;
+                // Nontemporal: the output is written once and not read here, so it does not displace
+                // the operand panels the other tiles still read from the caches.
+                typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+                __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(dst));
             } else {
                 const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
