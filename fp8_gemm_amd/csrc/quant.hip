@@ -441,7 +441,10 @@ struct WeightTileLds {
 // The body of one tile (bx, by) = (column tile, row tile), run by 256 threads with index tid.  Its
 // barriers are block-wide, so every thread of the block runs it (a second tile of a 512-thread
 // block, or an inactive one that loads and codes a valid tile and stores nothing).
-template <bool kBf16, bool kFp8, bool kVec>
+// kStream: nontemporal stores of the codes, for the weight preparation on its own, whose codes are
+// read later, by GEMMs of later calls (cached stores would only displace W from the caches); the
+// one-call preparation, whose GEMM follows at once, keeps them cached.
+template <bool kBf16, bool kFp8, bool kVec, bool kStream>
 __device__ __forceinline__ void weight_tile_body(const void* __restrict__ w, int64_t K, int64_t N,
                                                  const float* __restrict__ s, const float* __restrict__ w_scale,
                                                  int64_t scale_step, uint8_t* __restrict__ wq, int64_t bx, int64_t by,
@@ -492,7 +495,14 @@ __device__ __forceinline__ void weight_tile_body(const void* __restrict__ w, int
         const int c = idx / (kTJ / 16), t = idx % (kTJ / 16);
         const int64_t n = n0 + c, j = j0 + 16 * t;
         const uint4 u = *reinterpret_cast<const uint4*>(&tile[c * kTStride + 4 * (t ^ (2 * ((c >> 3) & 7)))]);
-        if (active && n < N && j < K) *reinterpret_cast<uint4*>(wq + n * K + j) = u;   // K % 16 == 0
+        if (active && n < N && j < K) {                                                  // K % 16 == 0
+            if constexpr (kStream) {
+                typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+                __builtin_nontemporal_store(v4u{u.x, u.y, u.z, u.w}, reinterpret_cast<v4u*>(wq + n * K + j));
+            } else {
+                *reinterpret_cast<uint4*>(wq + n * K + j) = u;
+            }
+        }
     }
 }
 
@@ -502,7 +512,7 @@ __global__ __launch_bounds__(256) void quant_weight_t_kernel(const void* __restr
                                                              const float* __restrict__ w_scale, int64_t scale_step,
                                                              uint8_t* __restrict__ wq) {
     __shared__ WeightTileLds L;
-    weight_tile_body<kBf16, kFp8, kVec>(w, K, N, s, w_scale, scale_step, wq, blockIdx.x, blockIdx.y, threadIdx.x, true,
+    weight_tile_body<kBf16, kFp8, kVec, true>(w, K, N, s, w_scale, scale_step, wq, blockIdx.x, blockIdx.y, threadIdx.x, true,
                                         L);
 }
 
@@ -527,7 +537,7 @@ __global__ __launch_bounds__(kActWaves * kWave) void quant_pair_kernel(
         const unsigned t = 2 * (blockIdx.x - nq) + half;
         const bool active = t < ntiles;
         const unsigned tc = active ? t : ntiles - 1;
-        weight_tile_body<kBf16, kFp8, true>(w, K, N, s, w_scale, 1, wq, tc % wtx, tc / wtx, threadIdx.x % 256, active,
+        weight_tile_body<kBf16, kFp8, true, false>(w, K, N, s, w_scale, 1, wq, tc % wtx, tc / wtx, threadIdx.x % 256, active,
                                             *L);
     }
 }
