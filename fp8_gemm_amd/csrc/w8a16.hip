@@ -285,7 +285,11 @@ __global__ __launch_bounds__(kGM * kGN * kWave, kBlocksPerCU) void w8a16_tile_ke
     constexpr int kThreads = kGM * kGN * kWave;
     constexpr int kXPer = (kXChunks + kThreads - 1) / kThreads, kWPer = (kWChunks + kThreads - 1) / kThreads;
     constexpr int kXStage = kBM * kRowBytes, kWStage = kBN * kRowBytes;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (kXStage + kWStage)];
+    // After the K loop the same LDS stages each wave's bf16 output tile (rows padded to kOutStride).
+    constexpr int kOutStride = kWN * 2 + 16;
+    constexpr int kOutBytes = kGM * kGN * kWM * kOutStride;
+    constexpr int kStageBytes = 2 * (kXStage + kWStage);
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kStageBytes > kOutBytes ? kStageBytes : kOutBytes];
     uint8_t* const xs = smem;
     uint8_t* const ws = smem + 2 * kXStage;
 
@@ -394,20 +398,48 @@ __global__ __launch_bounds__(kGM * kGN * kWave, kBlocksPerCU) void w8a16_tile_ke
     }
     if (t < nk) step(t, std::integral_constant<int, 0>{});
     // Lane results of block (i, j): row m = m0 + wm kWM + 32 i + r32, columns
-    // n = n0 + wn kWN + 32 j + 8 q + 4 g32 + r (r = 0..3) in acc[4 q + r].
+    // n = n0 + wn kWN + 32 j + 8 q + 4 g32 + r (r = 0..3) in acc[4 q + r].  They are scaled, rounded
+    // to bf16 and staged in LDS, then written as 16-byte pieces of whole output rows with
+    // nontemporal stores (the output is written once; cached stores would displace operand tiles
+    // that other blocks still read).
+    __syncthreads();                     // every wave has finished reading the stages
+    uint8_t* const ot = smem + wave * (kWM * kOutStride);
 #pragma unroll
     for (int j = 0; j < kNT; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int64_t n = n0 + wn * kWN + 32 * j + 8 * q + 4 * g32;
-            const v4f sc = load_scales4(w_scale, n, N);
+            const int col = 32 * j + 8 * q + 4 * g32;
+            const v4f sc = load_scales4(w_scale, n0 + wn * kWN + col, N);
 #pragma unroll
             for (int i = 0; i < kMT; ++i) {
-                const int64_t m = m0 + wm * kWM + 32 * i + r32;
-                const v4f a = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                store_w8a16(a, sc, m, n, M, N, y);
+                const int row = 32 * i + r32;
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r] * sc[r];
+                *reinterpret_cast<uint2*>(ot + row * kOutStride + col * 2) =
+                    make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
             }
         }
+    __syncthreads();                     // the staged rows are complete before they are read back
+    constexpr int kPieces = kWM * kWN * 2 / 16;
+    const int64_t mw0 = m0 + wm * kWM, nw0 = n0 + wn * kWN;
+#pragma unroll
+    for (int p = lane; p < kPieces; p += kWave) {
+        const int row = p / (kWN / 8), c = p % (kWN / 8);
+        const int64_t m = mw0 + row, n = nw0 + c * 8;
+        const uint4 v = *reinterpret_cast<const uint4*>(ot + row * kOutStride + c * 16);
+        if (m >= M) continue;
+        uint16_t* dst = y + m * N + n;
+        if ((N % 8) == 0 && n + 7 < N) {
+            typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+            __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(dst));
+        } else {
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (n + e < N) dst[e] = static_cast<uint16_t>(w4[e / 2] >> (16 * (e % 2)));
+        }
+    }
 }
 
 }  // namespace
