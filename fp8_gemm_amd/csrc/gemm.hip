@@ -200,6 +200,15 @@ __device__ __forceinline__ void copy_sv(const uint8_t* sbase, uint32_t voff, uin
         : "s"(lds), "v"(voff), "s"(sbase)
         : "memory", "m0");
 }
+// The same copy marked nontemporal, for data that is read once (a streamed weight matrix).
+__device__ __forceinline__ void copy_sv_nt(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "global_load_lds_dwordx4 %1, %2 nt"
+        :
+        : "s"(lds), "v"(voff), "s"(sbase)
+        : "memory", "m0");
+}
 __device__ __forceinline__ void copy_v(uintptr_t src, uint32_t lds) {
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
@@ -810,13 +819,15 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_kernel(
     // Copy i of this wave of a 16-row tile whose row r starts at src + row_off(r): row
     // r = (kCopies wave + i) / 4 of the tile, quarter q of the row; lane l fills stored chunk
     // 64 q + l, which holds logical chunk (64 q + l) ^ r.
-    auto copy_rows = [&](const uint8_t* src, auto row_off, uint8_t* dst) {
+    auto copy_rows = [&](const uint8_t* src, auto row_off, uint8_t* dst, auto stream) {
 #pragma unroll
         for (int i = 0; i < kCopies; ++i) {
             const int inst = kCopies * wave + i;
             const int r = inst >> 2, q = inst & 3;
             const uint32_t off = row_off(r) + static_cast<uint32_t>(((64 * q + lane) ^ r) * 16);
-            copy_sv(src, off, lds_addr(dst) + static_cast<uint32_t>(r * kDecodeLdsK + q * 1024));
+            const uint32_t l = lds_addr(dst) + static_cast<uint32_t>(r * kDecodeLdsK + q * 1024);
+            if constexpr (decltype(stream)::value) copy_sv_nt(src, off, l);    // W: read once
+            else copy_sv(src, off, l);
         }
     };
     // W rows from the block's own first row, so that offsets stay within the block's columns
@@ -827,7 +838,7 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_kernel(
             int64_t n = static_cast<int64_t>(t) * 16 + r;
             n = n < c1 - c0 ? n : c1 - c0 - 1;
             return static_cast<uint32_t>(n * K);
-        }, dst);
+        }, dst, std::true_type{});
     };
     // Fragment of row frag_row, K step s of this wave's eighth, from a tile in LDS.
     auto frag = [&](const uint8_t* b, int s) {
@@ -837,7 +848,7 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_kernel(
     // X goes through LDS too, next to tile 0: every global read of the kernel is then one of these
     // copies, whose waits are explicit (a plain load would make the compiler's own wait for it
     // count the copies issued after it, and wait for them as well).  X rows past M re-read row M - 1.
-    copy_rows(xq, [&](int r) { return static_cast<uint32_t>((r < M ? r : M - 1) * K); }, buf[1]);
+    copy_rows(xq, [&](int r) { return static_cast<uint32_t>((r < M ? r : M - 1) * K); }, buf[1], std::false_type{});
     copy_tile(0, buf[0]);
     wait_copies<kCopies>();                           // X has landed; tile 0 may be in flight
     block_barrier();
