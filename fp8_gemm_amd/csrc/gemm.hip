@@ -894,6 +894,124 @@ __global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_kernel(
     }
 }
 
+// The same weight stream for 16 < M <= 16 kMT rows (INT8, K = 4096): every wave keeps the X
+// fragments of its eighth of K for all kMT row tiles in registers (kMT 8 16-byte fragments), so a
+// weight tile in LDS feeds kMT matrix-core instructions per fragment read.  X is staged through the
+// two tile buffers first, two row tiles at a time; then the weight tiles stream as in
+// gemm_decode_lds_kernel, at most kDecodeMultiTiles of them per block.
+constexpr int kDecodeMultiTiles = 4;
+
+template <int kMT, bool kOutAcc>
+__global__ __launch_bounds__(kDecodeThreads) void gemm_decode_lds_multi_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ x_scale, const uint8_t* __restrict__ wq,
+    const float* __restrict__ w_scale, int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y,
+    void* __restrict__ out_acc, int tensor_scales, int cols) {
+    using MM = MmaI8x16;
+    using Acc = MM::Acc;
+    static_assert(kMT >= 2 && kMT % 2 == 0, "row tiles are staged two at a time");
+    constexpr int kWaves = kDecodeThreads / kWave;
+    constexpr int kS = kDecodeLdsK / kWaves / MM::kKStep;             // 8 instructions per wave and tile
+    constexpr int kTileBytes = 16 * kDecodeLdsK;
+    constexpr int kCopies = kTileBytes / 1024 / kWaves;               // 8 copies per wave and tile
+    static_assert(kDecodeMultiTiles * kWaves * kWave * kMT * static_cast<int>(sizeof(Acc)) <= 2 * kTileBytes,
+                  "the partial sums fit in the tile buffers");
+    __shared__ __attribute__((aligned(1024))) uint8_t buf[2][kTileBytes];
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int lane = threadIdx.x % kWave;
+    const int frag_row = lane & 15, frag_grp = lane >> 4;
+    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * cols;
+    const int64_t c1 = c0 + cols < N ? c0 + cols : N;
+    const int nt = static_cast<int>((c1 - c0 + 15) / 16);              // 1 .. kDecodeMultiTiles
+
+    // Copies of a 16-row tile as in gemm_decode_lds_kernel (chunks of each 256-byte group stored
+    // at chunk ^ (row mod 16)); `stream` marks the weight copies nontemporal.
+    auto copy_rows = [&](const uint8_t* src, auto row_off, uint8_t* dst, auto stream) {
+#pragma unroll
+        for (int i = 0; i < kCopies; ++i) {
+            const int inst = kCopies * wave + i;
+            const int r = inst >> 2, q = inst & 3;
+            const uint32_t off = row_off(r) + static_cast<uint32_t>(((64 * q + lane) ^ r) * 16);
+            const uint32_t l = lds_addr(dst) + static_cast<uint32_t>(r * kDecodeLdsK + q * 1024);
+            if constexpr (decltype(stream)::value) copy_sv_nt(src, off, l);
+            else copy_sv(src, off, l);
+        }
+    };
+    const uint8_t* const wblk = wq + c0 * K;
+    auto copy_tile = [&](int t, uint8_t* dst) {
+        copy_rows(wblk, [&](int r) {
+            int64_t n = static_cast<int64_t>(t) * 16 + r;
+            n = n < c1 - c0 ? n : c1 - c0 - 1;
+            return static_cast<uint32_t>(n * K);
+        }, dst, std::true_type{});
+    };
+    auto frag = [&](const uint8_t* b, int s) {
+        const int chunk = (wave * kS + s) * (MM::kKStep / 16) + frag_grp;
+        return *reinterpret_cast<const v4i*>(b + frag_row * kDecodeLdsK + ((chunk ^ frag_row) << 4));
+    };
+    // X: row tiles 2p and 2p + 1 through the two buffers; rows past M re-read row M - 1.
+    v4i fx[kMT][kS];
+#pragma unroll
+    for (int p = 0; p < kMT / 2; ++p) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int mt = 2 * p + h;
+            copy_rows(xq, [&](int r) {
+                const int64_t m = static_cast<int64_t>(mt) * 16 + r;
+                return static_cast<uint32_t>((m < M ? m : M - 1) * K);
+            }, buf[h], std::false_type{});
+        }
+        wait_copies<0>();
+        block_barrier();
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int s = 0; s < kS; ++s) fx[2 * p + h][s] = frag(buf[h], s);
+        wait_lds_reads();
+        block_barrier();                  // both buffers are free again
+    }
+    copy_tile(0, buf[0]);
+    if (nt > 1) copy_tile(1, buf[1]);
+    Acc acc[kDecodeMultiTiles][kMT];
+#pragma unroll
+    for (int t = 0; t < kDecodeMultiTiles; ++t)
+#pragma unroll
+        for (int i = 0; i < kMT; ++i) acc[t][i] = MM::zero();
+#pragma unroll
+    for (int t = 0; t < kDecodeMultiTiles; ++t) {
+        if (t >= nt) break;
+        if (t + 1 < nt) wait_copies<kCopies>();       // tile t landed; tile t + 1 may be in flight
+        else wait_copies<0>();
+        block_barrier();
+#pragma unroll
+        for (int s = 0; s < kS; ++s) {
+            const v4i w = frag(buf[t & 1], s);
+#pragma unroll
+            for (int i = 0; i < kMT; ++i) acc[t][i] = MM::run(&w, &fx[i][s], acc[t][i]);
+        }
+        wait_lds_reads();
+        block_barrier();                              // every wave has read buffer t & 1
+        if (t + 2 < nt) copy_tile(t + 2, buf[t & 1]);
+    }
+    // Partial sums of the 8 waves through LDS: [tile][row tile][wave][lane]; wave w adds and stores
+    // the (tile, row tile) pairs w, w + 8, ...
+    Acc* part = reinterpret_cast<Acc*>(&buf[0][0]);
+#pragma unroll
+    for (int t = 0; t < kDecodeMultiTiles; ++t)
+#pragma unroll
+        for (int i = 0; i < kMT; ++i)
+            if (t < nt) part[((t * kMT + i) * kWaves + wave) * kWave + lane] = acc[t][i];
+    wait_lds_reads();
+    block_barrier();
+    for (int ti = wave; ti < nt * kMT; ti += kWaves) {
+        Acc a = part[ti * kWaves * kWave + lane];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) a += part[(ti * kWaves + w) * kWave + lane];
+        const int t = ti / kMT, i = ti % kMT;
+        store_block<MM, kOutAcc>(a, static_cast<int64_t>(i) * 16, c0 + static_cast<int64_t>(t) * 16, lane, M, N,
+                                 x_scale, w_scale, tensor_scales != 0, y, out_acc, c1, N);
+    }
+}
+
 template <typename M16, typename MT, bool kOutAcc>
 hipError_t gemm_dispatch(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale,
                          int64_t M, int64_t N, int64_t K, uint16_t* y, void* out_acc, int tensor, hipStream_t st) {
@@ -919,6 +1037,24 @@ hipError_t gemm_dispatch(const uint8_t* xq, const float* x_scale, const uint8_t*
                                y, out_acc, tensor, cols);
         }
         return hipGetLastError();
+    }
+    if constexpr (M16::kChunks == 1) {
+        if (M <= 64 && K == kDecodeLdsK) {
+            // INT8, 16 < M <= 64, K = 4096: the weight stream of the decode kernel with 2 or 4 row
+            // tiles of X in registers; each block an equal range of columns (at most 4 tiles).
+            const int64_t units = (N + 7) / 8;
+            int64_t per = (units + kDecodeBlocks - 1) / kDecodeBlocks;
+            if (per > 2 * kDecodeMultiTiles) per = 2 * kDecodeMultiTiles;
+            const int cols = static_cast<int>(per * 8);
+            const dim3 g(static_cast<unsigned>((N + cols - 1) / cols)), b(kDecodeThreads);
+            if (M <= 32)
+                hipLaunchKernelGGL((gemm_decode_lds_multi_kernel<2, kOutAcc>), g, b, 0, st, xq, x_scale, wq, w_scale, M,
+                                   N, K, y, out_acc, tensor, cols);
+            else
+                hipLaunchKernelGGL((gemm_decode_lds_multi_kernel<4, kOutAcc>), g, b, 0, st, xq, x_scale, wq, w_scale, M,
+                                   N, K, y, out_acc, tensor, cols);
+            return hipGetLastError();
+        }
     }
     if (M <= 16 || (M <= 32 && N <= 8192)) {
         // A block per 16 output columns streams W once; X is re-read per block from L2, which is

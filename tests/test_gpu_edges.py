@@ -148,6 +148,19 @@ def test_decode_shapes(f, qtype, M, K, N):
     check_layer(run_layer(f, X, W, qtype=qtype), X, W, qtype=qtype)
 
 
+@pytest.mark.parametrize("M,N", [(17, 1000), (32, 9600), (33, 4100), (64, 14336), (48, 65560)])
+def test_decode_multi_row_tiles(f, M, N):
+    """INT8 with 16 < M <= 64 and K = 4096: the decode weight stream with 2 (M <= 32) or 4 row tiles
+    of X held in registers: a last row tile with rows past M; column ranges of 8 (one half tile), 40
+    (three tiles, the last a half), 24 (two, the last ragged), 56 (four, the last a half) and, past
+    256 x 64 columns, 64 (four whole tiles) with a last range of 24."""
+    K = 4096
+    announce(f"decode multi M={M} K={K} N={N} int8")
+    X = synth.random_matrix((M, K), seed=M + N, dtype="bf16", outliers=K // 100)
+    W = synth.random_matrix((K, N), seed=K + N, dtype="bf16", scale=0.02)
+    check_layer(run_layer(f, X, W, qtype="int8"), X, W, qtype="int8")
+
+
 def _pattern_codes(n, k):
     """INT8 weight codes in [-127, 127] that differ from row to row: ((31 n + 17 k + 5) mod 255) - 127."""
     return (n * 31 + k * 17 + 5) % 255 - 127
