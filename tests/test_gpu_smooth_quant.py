@@ -60,9 +60,12 @@ def check(f, X, W, alpha, qtype):
     np.testing.assert_array_equal(codes(g["xq"]), codes(qx))
 
 
-# (M, K, N): every activation register layout, ragged M and N, odd tile counts
+# (M, K, N): every activation register layout, ragged M and N, odd tile counts, a ragged last
+# column block of the calibration (K % 512 != 0) at 2048 and 2049 rows, and more weight scales to
+# zero than the calibration has threads (K = 64, N = 9000)
 SHAPES = [(1, 16, 8), (5, 48, 72), (33, 512, 520), (70, 1040, 136), (129, 2064, 264), (64, 4096, 200),
-          (19, 6160, 64), (40, 8192, 96), (3000, 256, 1032)]
+          (19, 6160, 64), (40, 8192, 96), (3000, 256, 1032),
+          (2048, 1040, 136), (2049, 528, 72), (127, 64, 9000)]
 
 
 @pytest.mark.parametrize("qtype", ["int8", "fp8"])
