@@ -270,28 +270,37 @@ __global__ __launch_bounds__(kThreads16) void w8a16_kernel(const uint16_t* __res
 // ------------------------------------------------------------------------------------------------
 typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kW8a16Big = 192;           // 256 x 256 tiles from this many on (three quarters of the CUs)
+constexpr int64_t kW8a16SplitK4Tiles = 256, kW8a16SplitK2Tiles = 512;   // 64 x 64 tiles split K 4 or 2 ways
 constexpr int kKS = 32;                  // k per step
 constexpr int kRowBytes = kKS * 2;       // bytes per row and step (bf16)
 
 __device__ __forceinline__ int tswz(int row, int chunk) { return row * kRowBytes + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
-template <int kBM, int kBN, int kGM, int kGN, int kBlocksPerCU>
-__global__ __launch_bounds__(kGM * kGN * kWave, kBlocksPerCU) void w8a16_tile_kernel(
+template <int kBM, int kBN, int kGM, int kGN, int kSK, int kBlocksPerCU>
+__global__ __launch_bounds__(kGM * kGN * kSK * kWave, kBlocksPerCU) void w8a16_tile_kernel(
     const uint16_t* __restrict__ x, const int8_t* __restrict__ wq, const float* __restrict__ w_scale, int64_t M,
     int64_t N, int64_t K, uint16_t* __restrict__ y, int tiles_m, int tiles_n) {
     constexpr int kWM = kBM / kGM, kWN = kBN / kGN;         // each wave's outputs
     constexpr int kMT = kWM / 32, kNT = kWN / 32;           // 32 x 32 blocks per wave along M and N
     constexpr int kXChunks = kBM * 4, kWChunks = kBN * 2;  // 16-byte X chunks, 16-code W chunks per step
-    constexpr int kThreads = kGM * kGN * kWave;
+    constexpr int kWavesMN = kGM * kGN;
+    constexpr int kThreads = kWavesMN * kWave;              // threads of one K group
     constexpr int kXPer = (kXChunks + kThreads - 1) / kThreads, kWPer = (kWChunks + kThreads - 1) / kThreads;
     constexpr int kXStage = kBM * kRowBytes, kWStage = kBN * kRowBytes;
-    // After the K loop the same LDS stages each wave's bf16 output tile (rows padded to kOutStride).
+    // After the K loop the same LDS takes the other K groups' accumulators, then each wave's bf16
+    // output tile (rows padded to kOutStride).
     constexpr int kOutStride = kWN * 2 + 16;
-    constexpr int kOutBytes = kGM * kGN * kWM * kOutStride;
+    constexpr int kOutBytes = kWavesMN * kWM * kOutStride;
     constexpr int kStageBytes = 2 * (kXStage + kWStage);
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kStageBytes > kOutBytes ? kStageBytes : kOutBytes];
-    uint8_t* const xs = smem;
-    uint8_t* const ws = smem + 2 * kXStage;
+    constexpr int kAccFloats = kMT * kNT * 16;
+    constexpr int kPartBytes = (kSK - 1) * kWavesMN * kAccFloats * kWave * 4;
+    constexpr int kSmem0 = kSK * kStageBytes > kOutBytes ? kSK * kStageBytes : kOutBytes;
+    constexpr int kSmem = kSmem0 > kPartBytes ? kSmem0 : kPartBytes;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
+    const int group = static_cast<int>(threadIdx.x) / kThreads;   // K group: K steps group, group + kSK, ...
+    const int tid = static_cast<int>(threadIdx.x) % kThreads;
+    uint8_t* const xs = smem + group * kStageBytes;
+    uint8_t* const ws = xs + 2 * kXStage;
 
     // XCD-aware order: consecutive block ids go to the 8 XCDs in turn; give each XCD a contiguous
     // range of tiles, walked 4 tile rows at a time, so the blocks sharing an L2 share operands.
@@ -304,7 +313,7 @@ __global__ __launch_bounds__(kGM * kGN * kWave, kBlocksPerCU) void w8a16_tile_ke
     const int in = bid % (kGroupM * tiles_n);
     const int64_t m0 = static_cast<int64_t>(first + in % gm) * kBM, n0 = static_cast<int64_t>(in / gm) * kBN;
 
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int wave = tid / kWave, lane = tid % kWave;
     const int wm = wave / kGN, wn = wave % kGN;
     const int r32 = lane % 32, g32 = lane / 32;
 
@@ -314,7 +323,7 @@ __global__ __launch_bounds__(kGM * kGN * kWave, kBlocksPerCU) void w8a16_tile_ke
     int xl[kXPer], xk[kXPer];
 #pragma unroll
     for (int i = 0; i < kXPer; ++i) {
-        const int p = min(static_cast<int>(threadIdx.x) + kThreads * i, kXChunks - 1), row = p / 4, c = p % 4;
+        const int p = min(tid + kThreads * i, kXChunks - 1), row = p / 4, c = p % 4;
         const int64_t gr = min(m0 + row, M - 1);
         xsrc[i] = x + gr * K + c * 8;
         xl[i] = tswz(row, c);
@@ -324,7 +333,7 @@ __global__ __launch_bounds__(kGM * kGN * kWave, kBlocksPerCU) void w8a16_tile_ke
     int wl[kWPer], wk[kWPer];
 #pragma unroll
     for (int i = 0; i < kWPer; ++i) {
-        const int p = min(static_cast<int>(threadIdx.x) + kThreads * i, kWChunks - 1), row = p / 2, h = p % 2;
+        const int p = min(tid + kThreads * i, kWChunks - 1), row = p / 2, h = p % 2;
         const int64_t gr = min(n0 + row, N - 1);
         wsrc[i] = wq + gr * K + h * 16;
         wl[i] = row;
@@ -332,7 +341,7 @@ __global__ __launch_bounds__(kGM * kGN * kWave, kBlocksPerCU) void w8a16_tile_ke
     }
     uint4 xr[2][kXPer], wr[2][kWPer];
     auto load = [&](int set, int t) {
-        const int64_t k0 = static_cast<int64_t>(t) * kKS;
+        const int64_t k0 = (static_cast<int64_t>(t) * kSK + group) * kKS;
 #pragma unroll
         for (int i = 0; i < kXPer; ++i)
             xr[set][i] = k0 + xk[i] < K ? *reinterpret_cast<const uint4*>(xsrc[i] + k0) : make_uint4(0u, 0u, 0u, 0u);
@@ -344,10 +353,10 @@ __global__ __launch_bounds__(kGM * kGN * kWave, kBlocksPerCU) void w8a16_tile_ke
     auto store = [&](int set, int stage) {
 #pragma unroll
         for (int i = 0; i < kXPer; ++i)
-            if (threadIdx.x + kThreads * i < kXChunks) *reinterpret_cast<uint4*>(xs + stage * kXStage + xl[i]) = xr[set][i];
+            if (tid + kThreads * i < kXChunks) *reinterpret_cast<uint4*>(xs + stage * kXStage + xl[i]) = xr[set][i];
 #pragma unroll
         for (int i = 0; i < kWPer; ++i) {
-            if (threadIdx.x + kThreads * i >= kWChunks) continue;
+            if (tid + kThreads * i >= kWChunks) continue;
             const int c0 = 2 * (wk[i] / 16);
             *reinterpret_cast<v8bf*>(ws + stage * kWStage + tswz(wl[i], c0)) =
                 codes_to_bf16(make_uint2(wr[set][i].x, wr[set][i].y));
@@ -362,7 +371,8 @@ __global__ __launch_bounds__(kGM * kGN * kWave, kBlocksPerCU) void w8a16_tile_ke
 #pragma unroll
         for (int j = 0; j < kNT; ++j) acc[i][j] = v16f{};
 
-    const int nk = static_cast<int>((K + kKS - 1) / kKS);
+    // Steps of this K group (all groups take the same count; steps past K load zeros).
+    const int nk = static_cast<int>(((K + kKS - 1) / kKS + kSK - 1) / kSK);
     // Register set t % 2 holds the loads of step t; LDS stage t % 2 the tile of step t.
     load(0, 0);
     if (nk > 1) load(1, 1);
@@ -402,25 +412,56 @@ __global__ __launch_bounds__(kGM * kGN * kWave, kBlocksPerCU) void w8a16_tile_ke
     // to bf16 and staged in LDS, then written as 16-byte pieces of whole output rows with
     // nontemporal stores (the output is written once; cached stores would displace operand tiles
     // that other blocks still read).
-    __syncthreads();                     // every wave has finished reading the stages
-    uint8_t* const ot = smem + wave * (kWM * kOutStride);
+    if constexpr (kSK > 1) {
+        // K groups 1.. hand their accumulators to group 0 through LDS, which adds them in group order
+        // (lane-major, so each access is 64 consecutive floats).
+        __syncthreads();                 // every wave has finished reading the stages
+        float* const part = reinterpret_cast<float*>(smem);
+        if (group > 0) {
+            float* const dst = part + ((group - 1) * kWavesMN + wave) * kAccFloats * kWave + lane;
 #pragma unroll
-    for (int j = 0; j < kNT; ++j)
+            for (int i = 0; i < kMT; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int col = 32 * j + 8 * q + 4 * g32;
-            const v4f sc = load_scales4(w_scale, n0 + wn * kWN + col, N);
+                for (int j = 0; j < kNT; ++j)
 #pragma unroll
-            for (int i = 0; i < kMT; ++i) {
-                const int row = 32 * i + r32;
-                float v[4];
+                    for (int e = 0; e < 16; ++e) dst[((i * kNT + j) * 16 + e) * kWave] = acc[i][j][e];
+        }
+        __syncthreads();
+        if (group == 0) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r] * sc[r];
-                *reinterpret_cast<uint2*>(ot + row * kOutStride + col * 2) =
-                    make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+            for (int g2 = 1; g2 < kSK; ++g2) {
+                const float* const src = part + ((g2 - 1) * kWavesMN + wave) * kAccFloats * kWave + lane;
+#pragma unroll
+                for (int i = 0; i < kMT; ++i)
+#pragma unroll
+                    for (int j = 0; j < kNT; ++j)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) acc[i][j][e] += src[((i * kNT + j) * 16 + e) * kWave];
             }
         }
+    }
+    __syncthreads();                     // every wave has finished reading the stages (and the partial sums)
+    uint8_t* const ot = smem + wave * (kWM * kOutStride);
+    if (group == 0) {                    // group 0 holds the sums; the other groups only meet the barrier
+#pragma unroll
+        for (int j = 0; j < kNT; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int col = 32 * j + 8 * q + 4 * g32;
+                const v4f sc = load_scales4(w_scale, n0 + wn * kWN + col, N);
+#pragma unroll
+                for (int i = 0; i < kMT; ++i) {
+                    const int row = 32 * i + r32;
+                    float v[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r] * sc[r];
+                    *reinterpret_cast<uint2*>(ot + row * kOutStride + col * 2) =
+                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                }
+            }
+    }
     __syncthreads();                     // the staged rows are complete before they are read back
+    if (group > 0) return;               // no barrier follows
     constexpr int kPieces = kWM * kWN * 2 / 16;
     const int64_t mw0 = m0 + wm * kWM, nw0 = n0 + wn * kWN;
 #pragma unroll
@@ -475,12 +516,18 @@ hipError_t launch_gemm_w8a16(const uint16_t* x, const int8_t* wq, const float* w
         hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(tm * tn)), dim3(threads), 0, st, x, wq, w_scale, M, N, K,
                            y, tm, tn);
     };
+    // 64 x 64 tiles that do not fill the chip twice over split K among 4 or 2 groups of waves.
+    const int64_t tiles64 = ((M + 63) / 64) * ((N + 63) / 64);
     if (((M + 255) / 256) * ((N + 255) / 256) >= kW8a16Big)
-        launch_tiled(w8a16_tile_kernel<256, 256, 2, 4, 1>, 256, 256, 512);
+        launch_tiled(w8a16_tile_kernel<256, 256, 2, 4, 1, 1>, 256, 256, 512);
     else if (((M + 127) / 128) * ((N + 127) / 128) >= 384)
-        launch_tiled(w8a16_tile_kernel<128, 128, 2, 2, 2>, 128, 128, 256);
+        launch_tiled(w8a16_tile_kernel<128, 128, 2, 2, 1, 2>, 128, 128, 256);
+    else if (tiles64 <= kW8a16SplitK4Tiles)
+        launch_tiled(w8a16_tile_kernel<64, 64, 2, 2, 4, 1>, 64, 64, 1024);
+    else if (tiles64 <= kW8a16SplitK2Tiles)
+        launch_tiled(w8a16_tile_kernel<64, 64, 2, 2, 2, 2>, 64, 64, 512);
     else
-        launch_tiled(w8a16_tile_kernel<64, 64, 2, 2, 2>, 64, 64, 256);
+        launch_tiled(w8a16_tile_kernel<64, 64, 2, 2, 1, 2>, 64, 64, 256);
     return hipGetLastError();
 }
 
