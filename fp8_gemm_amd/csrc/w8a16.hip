@@ -297,8 +297,9 @@ __global__ __launch_bounds__(kGM * kGN * kSK * kWave, kBlocksPerCU) void w8a16_t
     constexpr int kSmem0 = kSK * kStageBytes > kOutBytes ? kSK * kStageBytes : kOutBytes;
     constexpr int kSmem = kSmem0 > kPartBytes ? kSmem0 : kPartBytes;
     __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
-    const int group = static_cast<int>(threadIdx.x) / kThreads;   // K group: K steps group, group + kSK, ...
-    const int tid = static_cast<int>(threadIdx.x) % kThreads;
+    // K group: K steps group, group + kSK, ...  (0 when K is not split, known at compile time).
+    const int group = kSK == 1 ? 0 : static_cast<int>(threadIdx.x) / kThreads;
+    const int tid = kSK == 1 ? static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x) % kThreads;
     uint8_t* const xs = smem + group * kStageBytes;
     uint8_t* const ws = xs + 2 * kXStage;
 
@@ -313,7 +314,8 @@ __global__ __launch_bounds__(kGM * kGN * kSK * kWave, kBlocksPerCU) void w8a16_t
     const int in = bid % (kGroupM * tiles_n);
     const int64_t m0 = static_cast<int64_t>(first + in % gm) * kBM, n0 = static_cast<int64_t>(in / gm) * kBN;
 
-    const int wave = tid / kWave, lane = tid % kWave;
+    const unsigned utid = static_cast<unsigned>(tid);
+    const int wave = utid / kWave, lane = utid % kWave;
     const int wm = wave / kGN, wn = wave % kGN;
     const int r32 = lane % 32, g32 = lane / 32;
 
