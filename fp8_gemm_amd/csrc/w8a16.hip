@@ -271,6 +271,9 @@ __global__ __launch_bounds__(kThreads16) void w8a16_kernel(const uint16_t* __res
 typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kW8a16Big = 192;           // 256 x 256 tiles from this many on (three quarters of the CUs)
 constexpr int64_t kW8a16SplitK4Tiles = 256, kW8a16SplitK2Tiles = 512;   // 64 x 64 tiles split K 4 or 2 ways
+// 128 x 128 tiles with K split 2 ways (one block of 8 waves per CU) from 160 to 256 of them: fewer
+// leave too many CUs idle, more need a second round of blocks.
+constexpr int64_t kW8a16Split128Min = 160, kW8a16Split128Max = 256;
 constexpr int kKS = 32;                  // k per step
 constexpr int kRowBytes = kKS * 2;       // bytes per row and step (bf16)
 
@@ -518,12 +521,15 @@ hipError_t launch_gemm_w8a16(const uint16_t* x, const int8_t* wq, const float* w
         hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(tm * tn)), dim3(threads), 0, st, x, wq, w_scale, M, N, K,
                            y, tm, tn);
     };
-    // 64 x 64 tiles that do not fill the chip twice over split K among 4 or 2 groups of waves.
-    const int64_t tiles64 = ((M + 63) / 64) * ((N + 63) / 64);
+    // 64 x 64 tiles that do not fill the chip twice over split K among 4 or 2 groups of waves, and
+    // so do 128 x 128 tiles that fill most of it once.
+    const int64_t tiles64 = ((M + 63) / 64) * ((N + 63) / 64), tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
     if (((M + 255) / 256) * ((N + 255) / 256) >= kW8a16Big)
         launch_tiled(w8a16_tile_kernel<256, 256, 2, 4, 1, 1>, 256, 256, 512);
-    else if (((M + 127) / 128) * ((N + 127) / 128) >= 384)
+    else if (tiles128 >= 384)
         launch_tiled(w8a16_tile_kernel<128, 128, 2, 2, 1, 2>, 128, 128, 256);
+    else if (tiles128 >= kW8a16Split128Min && tiles128 <= kW8a16Split128Max)
+        launch_tiled(w8a16_tile_kernel<128, 128, 2, 2, 2, 1>, 128, 128, 512);
     else if (tiles64 <= kW8a16SplitK4Tiles)
         launch_tiled(w8a16_tile_kernel<64, 64, 2, 2, 4, 1>, 64, 64, 1024);
     else if (tiles64 <= kW8a16SplitK2Tiles)

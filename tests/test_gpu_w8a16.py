@@ -12,7 +12,7 @@ Shapes cover the decode kernel (M <= 16, K = 4096), the small-M kernel (up to 12
 layers), and the tiled kernel with 64 x 64, 128 x 128 and 256 x 256 tiles (ragged M and N, fewer
 rows than one tile, a K that ends in half a 32-wide step, a grid that does not divide into the 8
 XCDs), 64 x 64 tiles with K split among 4 groups of waves (at most 256 tiles) and among 2 (at most
-512), whose partial sums meet in LDS.
+512), and 128 x 128 tiles with K split among 2 (160 to 256 tiles), whose partial sums meet in LDS.
 """
 import numpy as np
 import pytest
@@ -39,7 +39,8 @@ SHAPES = [(1, 4096, 1000), (7, 4096, 4100), (16, 4096, 96), (5, 528, 77), (40, 1
           (129, 2064, 517), (17, 48, 33), (100, 528, 8200), (1000, 1040, 1000), (2050, 272, 4100),
           (4096, 4096, 4096),
           (3000, 1040, 4200), (2600, 272, 5100),   # 256 x 256 tiles: ragged M, N and K, 220 blocks
-          (64, 4096, 9000), (400, 1040, 4104)]     # 64 x 64 tiles with K split 4 and 2 ways
+          (64, 4096, 9000), (400, 1040, 4104),     # 64 x 64 tiles with K split 4 and 2 ways
+          (1000, 1040, 3000), (300, 2064, 9000)]   # 128 x 128 tiles with K split 2 ways
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
