@@ -267,6 +267,10 @@ __global__ __launch_bounds__(kThreads16) void w8a16_kernel(const uint16_t* __res
 // loads: the loads of step t + 2 go out when step t starts, and step t + 1's (loaded during step
 // t - 1) are written to LDS when step t ends, so each load has two steps to land.  Rows past M or
 // N re-read the last row (never stored); the k past K (K % 32 = 16) are zero.
+// With kSK > 1 the block holds kSK groups of kGM x kGN waves, each with its own two stages, for
+// shapes with too few tiles to keep the CUs' waves busy: group g takes K steps g, g + kSK, ..., and
+// at the end groups 1.. hand their accumulators to group 0 through LDS, which adds them in group
+// order (an fp32 sum whose order depends on the split, not on the run).
 // ------------------------------------------------------------------------------------------------
 typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kW8a16Big = 192;           // 256 x 256 tiles from this many on (three quarters of the CUs)
